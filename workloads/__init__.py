@@ -1,0 +1,39 @@
+"""Seeded synthetic inputs and the host block manager.
+
+Shared by the device path's tests/bench and the oracle's tests; holds no
+attention or cache-write arithmetic.
+"""
+
+from .blockpool import BlockPool, PoolExhausted, Sequence
+from .configs import (
+    BUILDERS,
+    ELEM_BYTES,
+    Workload,
+    build,
+    custom,
+    llama3_8b_b32,
+    long_ctx_fp8_b8,
+    mha_b32_ctx4096,
+    shared_prefix_cow_b64,
+    tiny_fp32_gqa2,
+    permute_physical,
+    unshare,
+)
+
+__all__ = [
+    "BlockPool",
+    "PoolExhausted",
+    "Sequence",
+    "BUILDERS",
+    "ELEM_BYTES",
+    "Workload",
+    "build",
+    "custom",
+    "llama3_8b_b32",
+    "long_ctx_fp8_b8",
+    "mha_b32_ctx4096",
+    "shared_prefix_cow_b64",
+    "tiny_fp32_gqa2",
+    "permute_physical",
+    "unshare",
+]
