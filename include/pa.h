@@ -1,0 +1,235 @@
+/*
+ * pa.h -- C ABI of libpa: paged-attention decode and its cache operations on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (restated from the pages; see each entry point):
+ *
+ *   - Attention is softmax(q K^T / sqrt(d_k)) V ("KV-Cache evolution",
+ *     smallfiredragon.com, section 1). In decode, each sequence contributes
+ *     one new query token that attends over all of its cached tokens ("vLLM
+ *     inference principles", krshare.site, section on the two phases).
+ *   - Grouped-query attention: query heads come in groups that share one K/V
+ *     head ("KV-Cache evolution", section 3A). Query head h reads KV head
+ *     h / (num_q_heads / num_kv_heads) (contiguous groups).
+ *   - The KV cache is cut into fixed-size physical blocks; a per-sequence
+ *     block table maps logical block j (tokens j*block_size ... in sequence
+ *     order) to a physical block id ("PagedAttention deep dive", juejin.cn,
+ *     section 2.1; "vLLM inference principles", block-table figure).
+ *   - New tokens are written into the slot the host block manager assigned
+ *     ("PagedAttention deep dive", section 2.2), and a block shared by several
+ *     sequences is copied before one of them writes a different token into it
+ *     (copy-on-write, "PagedAttention deep dive", section 2.3; "KV-cache
+ *     sharing article", intelliparadigm.com, section 3.1).
+ *
+ * Conventions shared by every entry point:
+ *
+ *   - Every data pointer is a DEVICE pointer to contiguous row-major memory
+ *     owned by the caller. The library borrows it for the work it enqueues
+ *     and keeps no reference afterwards; the caller keeps it alive until the
+ *     stream has passed that work. The library allocates no memory, holds no
+ *     global state and is reentrant.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. All work is enqueued asynchronously on it.
+ *   - Cache layout: k_cache and v_cache are [num_blocks, block_size,
+ *     num_kv_heads, head_dim], so one token's row of one KV head is head_dim
+ *     contiguous elements.
+ *   - Everything that can be checked on the host is checked before anything
+ *     is enqueued, and a failed check returns a status without side effects.
+ *     Contract breaches that live in device memory are NOT checked (block ids
+ *     outside [0, num_blocks), context lengths above max_blocks_per_seq *
+ *     block_size, duplicate slots in one call, overlapping copy pairs): their
+ *     result is undefined.
+ *   - A launch failure reported by the runtime returns PA_ERR_LAUNCH.
+ *
+ * Supported configurations: head_dim 64 or 128; block_size 16; any
+ * num_q_heads that is a multiple of num_kv_heads; (q, kv) element types
+ * (f32, f32), (f16, f16), (bf16, bf16), (f16, fp8_e4m3fn), (bf16, fp8_e4m3fn).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                         */
+  PA_ERR_BAD_SHAPE = 2,         /* a size is negative/zero where it may not be, or    */
+                                /* sizes are inconsistent (Hq % Hkv != 0, ...)        */
+  PA_ERR_UNSUPPORTED = 3,       /* valid but not built: head_dim, block_size, dtypes  */
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PA_ERR_LAUNCH = 5             /* the HIP runtime refused a kernel launch            */
+} pa_status;
+
+/* Element types. fp8_e4m3fn is OCP E4M3FN (bias 7, max 448, no infinities). */
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3FN = 3
+} pa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *pa_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int pa_version(void);
+
+/*
+ * Number of partitions a split-context decode uses for a block table of
+ * max_blocks_per_seq entries: ceil(max_blocks_per_seq * block_size /
+ * partition_size). Returns 0 for partition_size <= 0.
+ */
+int pa_num_partitions(int max_blocks_per_seq, int block_size, int partition_size);
+
+/*
+ * Bytes of device workspace pa_decode needs: 0 when partition_size == 0
+ * (single pass), otherwise the split partials of pa_decode_partials:
+ * num_seqs * num_q_heads * NP * (head_dim + 2) * 4, NP as above.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                int max_blocks_per_seq, int block_size,
+                                int partition_size);
+
+/*
+ * pa_decode -- one decode step of paged attention.
+ *
+ * For every sequence b and query head h, with n = context_lens[b] and
+ * g = h / (num_q_heads / num_kv_heads):
+ *
+ *   s_j     = scale * k_scale * < q[b, h, :], K[j] >        for j < n,
+ *   out[b,h] = v_scale * sum_j exp(s_j - max s) V[j] / sum_j exp(s_j - max s),
+ *
+ * where K[j] / V[j] is row (block_tables[b, j / block_size], j % block_size,
+ * g, :) of k_cache / v_cache. A sequence with n == 0 gets out[b] = 0.
+ * Sources: the attention formula ("KV-Cache evolution", section 1); the
+ * block-table gather ("PagedAttention deep dive", section 2.1; "vLLM
+ * inference principles", block-table figure); fp8 storage of the cache
+ * ("PagedAttention deep dive", sections 3.2 and 4; "KV-Cache evolution",
+ * section 3C) with per-tensor scales k_scale / v_scale (ignored unless
+ * kv_dtype is PA_FP8_E4M3FN).
+ *
+ *   out           [num_seqs, num_q_heads, head_dim], q_dtype; must not alias
+ *                 any input.
+ *   q             [num_seqs, num_q_heads, head_dim], q_dtype.
+ *   k_cache/v_cache [num_blocks, block_size, num_kv_heads, head_dim], kv_dtype;
+ *                 never written.
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; only the first
+ *                 ceil(n / block_size) entries of row b are read.
+ *   context_lens  [num_seqs] int32, each in [0, max_blocks_per_seq*block_size].
+ *   scale         softmax scale, normally 1/sqrt(head_dim).
+ *   partition_size 0: one pass over the whole context per (sequence, KV
+ *                 head). > 0 (a multiple of block_size): split-context
+ *                 decode -- pa_decode_partials into `workspace`, then
+ *                 pa_decode_reduce into `out` (same stream).
+ *   workspace     device buffer of at least pa_decode_workspace_size(...)
+ *                 bytes when partition_size > 0 (may be NULL otherwise). Its
+ *                 contents on entry do not matter; one call at a time may use
+ *                 a given workspace.
+ */
+pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens,
+                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, int max_blocks_per_seq,
+                    float scale, int q_dtype, int kv_dtype, float k_scale, float v_scale,
+                    int partition_size, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * pa_decode_partials -- the per-partition half of split-context decode.
+ *
+ * Partition p of sequence b covers logical tokens [p*P, min((p+1)*P, n)),
+ * P = partition_size (a multiple of block_size), n = context_lens[b]. For
+ * each (b, h, p) with p < ceil(n / P) it writes, in float32,
+ *
+ *   max_logits[b, h, p] = m = max_j s_j                     (s_j as in pa_decode)
+ *   exp_sums[b, h, p]   = l = sum_j exp(s_j - m)
+ *   tmp_out[b, h, p, :] =     sum_j exp(s_j - m) * v_scale * V[j] / l
+ *
+ * Entries with p >= ceil(n / P) are not written. Merging the partials of a
+ * sequence (pa_decode_reduce) gives the same attention as pa_decode; the
+ * partials of one sequence may also be produced on different devices and
+ * merged afterwards.
+ *
+ *   tmp_out      [num_seqs, num_q_heads, max_partitions, head_dim] float32
+ *   max_logits   [num_seqs, num_q_heads, max_partitions] float32
+ *   exp_sums     [num_seqs, num_q_heads, max_partitions] float32
+ *   max_partitions >= pa_num_partitions(max_blocks_per_seq, block_size, P).
+ * Other arguments as in pa_decode.
+ */
+pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
+                             int max_partitions, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             int max_blocks_per_seq, float scale, int q_dtype, int kv_dtype,
+                             float k_scale, float v_scale, int partition_size, void *stream);
+
+/*
+ * pa_decode_reduce -- merge split-context partials into the decode output.
+ *
+ * For each (b, h), over the first ceil(n / P) partitions: M = max_p m_p,
+ * w_p = l_p * exp(m_p - M), out[b, h] = sum_p w_p * tmp_out[b, h, p] /
+ * sum_p w_p, rounded to out_dtype (round to nearest even). n == 0 gives 0.
+ *
+ *   out          [num_seqs, num_q_heads, head_dim], out_dtype (f32, f16, bf16)
+ *   tmp_out, max_logits, exp_sums, max_partitions: as written by
+ *                pa_decode_partials with the same partition_size.
+ */
+pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_logits,
+                           const float *exp_sums, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int head_dim, int max_partitions,
+                           int partition_size, int out_dtype, void *stream);
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K/V rows into their slots.
+ *
+ * For each token t with s = slot_mapping[t] >= 0:
+ *   k_cache[s / block_size, s % block_size, :, :] = enc(key[t, :, :], k_scale)
+ *   v_cache[s / block_size, s % block_size, :, :] = enc(value[t, :, :], v_scale)
+ * enc is a bit copy when cache_dtype == src_dtype; for an fp8 cache it is
+ * E4M3FN(float32(x) / scale) with a correctly rounded float32 division,
+ * round-to-nearest-even and saturation to +-448 (NaN -> 0x7F | sign).
+ * Tokens with a negative slot are skipped. Sources: "PagedAttention deep
+ * dive", section 2.2 (a sequence fills its current block, then a new one);
+ * "vLLM inference principles", two phases (decode extends the cache).
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim], src_dtype (f32, f16,
+ *                 bf16)
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim],
+ *                 cache_dtype == src_dtype, or PA_FP8_E4M3FN from f16/bf16/f32
+ *   slot_mapping  [num_tokens] int64, slots distinct among non-negative entries
+ * num_tokens == 0 is a no-op (key, value and slot_mapping may then be NULL).
+ */
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache,
+                               void *v_cache, const int64_t *slot_mapping, int num_tokens,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               int src_dtype, int cache_dtype, float k_scale, float v_scale,
+                               void *stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block copies.
+ *
+ * For each pair i: k_cache[dst_i] = k_cache[src_i] and v_cache[dst_i] =
+ * v_cache[src_i], bit for bit, where (src_i, dst_i) = block_mapping[i, :].
+ * Destinations must be distinct and never a source of the same call (the
+ * result then does not depend on pair order). Sources: "PagedAttention deep
+ * dive", section 2.3; "KV-cache sharing article", section 3.1.
+ *
+ *   block_mapping [num_pairs, 2] int64, device memory
+ *   cache_dtype   element type of both caches (only its size matters)
+ * num_pairs == 0 is a no-op (block_mapping may then be NULL).
+ */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int cache_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

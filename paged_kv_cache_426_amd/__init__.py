@@ -1,0 +1,253 @@
+"""Paged-attention decode on MI355X (gfx950): Python face of libpa.
+
+A thin ctypes binding over the C ABI declared in ``include/pa.h``. It only
+checks and marshals arguments (device pointers, sizes, element-type codes and
+the current HIP stream); every step of the computation runs in libpa's HIP
+kernels. PyTorch provides device memory and streams.
+
+There is no CPU fallback: calling any operation with tensors that are not on
+a GPU, or without the built library, raises.
+"""
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN",
+    "PaError", "lib", "library_path", "dtype_code",
+    "decode", "decode_partials", "decode_reduce", "decode_workspace_size",
+    "num_partitions", "reshape_and_cache", "copy_blocks",
+]
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2, 3
+
+_DTYPES = {
+    torch.float32: PA_F32,
+    torch.float16: PA_F16,
+    torch.bfloat16: PA_BF16,
+    torch.float8_e4m3fn: PA_FP8_E4M3FN,
+    torch.uint8: PA_FP8_E4M3FN,  # raw E4M3FN codes
+}
+_TORCH_OF = {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class PaError(RuntimeError):
+    """A libpa call returned a non-zero status."""
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpa.so")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpa. Built from source first if no built library exists."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            from .build import build
+
+            build()
+        L = ctypes.CDLL(path)
+        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_size_t)
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_status_string.argtypes = [i32]
+        L.pa_version.restype = i32
+        L.pa_num_partitions.restype = i32
+        L.pa_num_partitions.argtypes = [i32, i32, i32]
+        L.pa_decode_workspace_size.restype = sz
+        L.pa_decode_workspace_size.argtypes = [i32] * 6
+        L.pa_decode.restype = i32
+        L.pa_decode.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, f32, f32, i32, vp, sz, vp]
+        L.pa_decode_partials.restype = i32
+        L.pa_decode_partials.argtypes = ([vp] * 3 + [i32] + [vp] * 5 + [i32] * 7 +
+                                         [f32, i32, i32, f32, f32, i32, vp])
+        L.pa_decode_reduce.restype = i32
+        L.pa_decode_reduce.argtypes = [vp] * 5 + [i32] * 6 + [vp]
+        L.pa_reshape_and_cache.restype = i32
+        L.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 7 + [f32, f32, vp]
+        L.pa_copy_blocks.restype = i32
+        L.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PaError(f"libpa: {lib().pa_status_string(status).decode()} (status {status})")
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise PaError(f"unsupported element type {t.dtype}") from None
+
+
+def _dev(*tensors) -> torch.device:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise PaError("libpa operations take GPU tensors only (no CPU path)")
+        if not t.is_contiguous():
+            raise PaError("libpa operations take contiguous tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise PaError("all tensors must be on the same GPU")
+    return dev
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _i32(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.int32:
+        raise PaError(f"{name} must be int32")
+
+
+def _i64(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.int64:
+        raise PaError(f"{name} must be int64")
+
+
+def num_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
+    return lib().pa_num_partitions(max_blocks_per_seq, block_size, partition_size)
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
+                          max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
+    return lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                                          block_size, partition_size)
+
+
+def _decode_shapes(q, k_cache, v_cache, block_tables, context_lens):
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise PaError("expected q [B, Hq, d] and caches [num_blocks, block_size, Hkv, d]")
+    B, Hq, d = q.shape
+    NB, bs, Hkv, d2 = k_cache.shape
+    if d2 != d or block_tables.dim() != 2 or block_tables.shape[0] != B or \
+            context_lens.shape != (B,):
+        raise PaError("inconsistent shapes among q, caches, block_tables, context_lens")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    return B, Hq, d, NB, bs, Hkv, block_tables.shape[1]
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: Optional[float] = None,
+           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+           out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged-attention decode (C: pa_decode). Returns out [B, Hq, d] in q's type."""
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PaError("out must match q in shape and type")
+    need = decode_workspace_size(B, Hq, d, MBS, bs, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                           _ptr(context_lens), B, Hq, Hkv, d, bs, NB, MBS, float(scale),
+                           dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
+                           int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def decode_partials(q, k_cache, v_cache, block_tables, context_lens, partition_size: int,
+                    scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                    tmp_out=None, max_logits=None, exp_sums=None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Split-context partials (C: pa_decode_partials): returns
+    (tmp_out [B, Hq, NP, d], max_logits [B, Hq, NP], exp_sums [B, Hq, NP]), float32."""
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, tmp_out, max_logits, exp_sums)
+    B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    NP = num_partitions(MBS, bs, partition_size)
+    if tmp_out is None:
+        tmp_out = torch.empty((B, Hq, NP, d), dtype=torch.float32, device=dev)
+        max_logits = torch.empty((B, Hq, NP), dtype=torch.float32, device=dev)
+        exp_sums = torch.empty((B, Hq, NP), dtype=torch.float32, device=dev)
+    for t in (tmp_out, max_logits, exp_sums):
+        if t.dtype != torch.float32:
+            raise PaError("partials are float32")
+    if tmp_out.dim() != 4 or tmp_out.shape[:2] != (B, Hq) or tmp_out.shape[3] != d or \
+            max_logits.shape != tmp_out.shape[:3] or exp_sums.shape != tmp_out.shape[:3]:
+        raise PaError("partials have the wrong shape")
+    _check(lib().pa_decode_partials(_ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+                                    tmp_out.shape[2], _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs,
+                                    NB, MBS, float(scale), dtype_code(q), dtype_code(k_cache),
+                                    float(k_scale), float(v_scale), int(partition_size),
+                                    _stream(dev)))
+    return tmp_out, max_logits, exp_sums
+
+
+def decode_reduce(tmp_out, max_logits, exp_sums, context_lens, partition_size: int,
+                  out_dtype: torch.dtype = torch.bfloat16,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Merge split partials (C: pa_decode_reduce). Returns out [B, Hq, d]."""
+    dev = _dev(tmp_out, max_logits, exp_sums, context_lens, out)
+    _i32(context_lens, "context_lens")
+    B, Hq, NP, d = tmp_out.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
+    if out.dtype not in _TORCH_OF.values() or out.shape != (B, Hq, d):
+        raise PaError("out must be [B, Hq, d] float32, float16 or bfloat16")
+    _check(lib().pa_decode_reduce(_ptr(out), _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+                                  _ptr(context_lens), B, Hq, d, NP, int(partition_size),
+                                  dtype_code(out), _stream(dev)))
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
+                      v_scale: float = 1.0) -> None:
+    """Write new tokens' K/V rows into their slots (C: pa_reshape_and_cache)."""
+    dev = _dev(key, value, k_cache, v_cache, slot_mapping)
+    _i64(slot_mapping, "slot_mapping")
+    if key.dim() != 3 or value.shape != key.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or key.shape[1:] != k_cache.shape[2:] or \
+            slot_mapping.shape != (key.shape[0],) or value.dtype != key.dtype or \
+            v_cache.dtype != k_cache.dtype:
+        raise PaError("expected key/value [N, Hkv, d], caches [num_blocks, bs, Hkv, d], slots [N]")
+    N, Hkv, d = key.shape
+    NB, bs = k_cache.shape[:2]
+    _check(lib().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(slot_mapping), N, Hkv, d, bs, NB, dtype_code(key),
+                                      dtype_code(k_cache), float(k_scale), float(v_scale),
+                                      _stream(dev)))
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy-on-write block copies (C: pa_copy_blocks); block_mapping [P, 2] int64 (src, dst)."""
+    dev = _dev(k_cache, v_cache, block_mapping)
+    _i64(block_mapping, "block_mapping")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2 or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise PaError("expected caches [num_blocks, bs, Hkv, d] and block_mapping [P, 2]")
+    NB, bs, Hkv, d = k_cache.shape
+    _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                                block_mapping.shape[0], Hkv, d, bs, NB, dtype_code(k_cache),
+                                _stream(dev)))

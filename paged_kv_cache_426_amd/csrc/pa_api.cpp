@@ -1,0 +1,246 @@
+// C ABI of libpa: argument validation and dispatch to the gfx950 kernels.
+// Every check that can be made on the host happens here, before anything is
+// enqueued; a failed check returns a status and has no side effects.
+
+#include <limits.h>
+#include <math.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kSupportedBlockSize = 16;
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+bool known_dtype(int t) {
+  return t == PA_F32 || t == PA_F16 || t == PA_BF16 || t == PA_FP8_E4M3FN;
+}
+
+int elem_bytes(int t) { return t == PA_F32 ? 4 : t == PA_FP8_E4M3FN ? 1 : 2; }
+
+bool supported_decode_pair(int q, int kv) {
+  if (q == kv) return q == PA_F32 || q == PA_F16 || q == PA_BF16;
+  return kv == PA_FP8_E4M3FN && (q == PA_F16 || q == PA_BF16);
+}
+
+pa_status status_of(int hip_err) { return hip_err == 0 ? PA_OK : PA_ERR_LAUNCH; }
+
+// Shared checks of pa_decode and pa_decode_partials.
+pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, int max_blocks_per_seq, float scale, int q_dtype,
+                       int kv_dtype, float k_scale, float v_scale, int partition_size) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (!known_dtype(q_dtype) || !known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || block_size != kSupportedBlockSize ||
+      !supported_decode_pair(q_dtype, kv_dtype))
+    return PA_ERR_UNSUPPORTED;
+  if (partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (kv_dtype == PA_FP8_E4M3FN && (!isfinite(k_scale) || !isfinite(v_scale)))
+    return PA_ERR_BAD_SHAPE;
+  // launch-grid and in-kernel 32-bit offset limits
+  const long long row_bytes = (long long)num_kv_heads * head_dim * elem_bytes(kv_dtype);
+  if (row_bytes * block_size >= INT_MAX) return PA_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  const long long grid_y = (long long)num_kv_heads * (group / pa::heads_per_workgroup(group));
+  if (grid_y > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case PA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int pa_version(void) { return 100; }
+
+int pa_num_partitions(int max_blocks_per_seq, int block_size, int partition_size) {
+  if (partition_size <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
+  const long long tokens = (long long)max_blocks_per_seq * block_size;
+  return (int)((tokens + partition_size - 1) / partition_size);
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                int max_blocks_per_seq, int block_size, int partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const size_t np = (size_t)pa_num_partitions(max_blocks_per_seq, block_size, partition_size);
+  return (size_t)num_seqs * num_q_heads * np * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
+                             int max_partitions, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             int max_blocks_per_seq, float scale, int q_dtype, int kv_dtype,
+                             float k_scale, float v_scale, int partition_size, void *stream) {
+  if (!tmp_out || !max_logits || !exp_sums) return PA_ERR_NULL_POINTER;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                              max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                              partition_size);
+  if (st != PA_OK) return st;
+  if (partition_size == 0) return PA_ERR_BAD_SHAPE;
+  if (max_partitions < pa_num_partitions(max_blocks_per_seq, block_size, partition_size))
+    return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeLaunch a{};
+  a.tmp_out = tmp_out;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.max_partitions = max_partitions;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  a.partition_size = partition_size;
+  return status_of(pa::launch_decode(a, stream));
+}
+
+pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_logits,
+                           const float *exp_sums, const int32_t *context_lens, int num_seqs,
+                           int num_q_heads, int head_dim, int max_partitions, int partition_size,
+                           int out_dtype, void *stream) {
+  if (!out || !tmp_out || !max_logits || !exp_sums || !context_lens) return PA_ERR_NULL_POINTER;
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_partitions <= 0 ||
+      partition_size <= 0)
+    return PA_ERR_BAD_SHAPE;
+  if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535 || num_q_heads > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  return status_of(pa::launch_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs,
+                                     num_q_heads, head_dim, max_partitions, partition_size,
+                                     out_dtype, stream));
+}
+
+pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, int max_blocks_per_seq, float scale, int q_dtype,
+                    int kv_dtype, float k_scale, float v_scale, int partition_size,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!out) return PA_ERR_NULL_POINTER;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                              max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                              partition_size);
+  if (st != PA_OK) return st;
+  if (partition_size > 0) {
+    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+                                                 max_blocks_per_seq, block_size, partition_size);
+    if (!workspace && need > 0) return PA_ERR_NULL_POINTER;
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (partition_size == 0) {
+    pa::DecodeLaunch a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale = scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv_dtype;
+    a.partition_size = 0;
+    return status_of(pa::launch_decode(a, stream));
+  }
+  // split context: partials into the workspace, then the merge
+  const int np = pa_num_partitions(max_blocks_per_seq, block_size, partition_size);
+  const size_t nbh = (size_t)num_seqs * num_q_heads * np;
+  float *tmp_out = static_cast<float *>(workspace);
+  float *max_logits = tmp_out + nbh * head_dim;
+  float *exp_sums = max_logits + nbh;
+  st = pa_decode_partials(tmp_out, max_logits, exp_sums, np, q, k_cache, v_cache, block_tables,
+                          context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, scale, q_dtype, kv_dtype,
+                          k_scale, v_scale, partition_size, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs,
+                          num_q_heads, head_dim, np, partition_size, q_dtype, stream);
+}
+
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache, void *v_cache,
+                               const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks, int src_dtype,
+                               int cache_dtype, float k_scale, float v_scale, void *stream) {
+  if (num_tokens == 0 && k_cache && v_cache) return PA_OK;  // no-op; token arrays may be empty
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_BAD_SHAPE;
+  if (!known_dtype(src_dtype) || !known_dtype(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  if (src_dtype == PA_FP8_E4M3FN) return PA_ERR_UNSUPPORTED;
+  if (src_dtype != cache_dtype && cache_dtype != PA_FP8_E4M3FN) return PA_ERR_UNSUPPORTED;
+  if (cache_dtype == PA_FP8_E4M3FN && src_dtype != cache_dtype &&
+      (!isfinite(k_scale) || !isfinite(v_scale) || k_scale == 0.0f || v_scale == 0.0f))
+    return PA_ERR_BAD_SHAPE;
+  // rows are moved in 16-byte pieces of the source
+  const long long row_src_bytes = (long long)num_kv_heads * head_dim * elem_bytes(src_dtype);
+  if (row_src_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (row_src_bytes > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  return status_of(pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+                                                num_tokens, num_kv_heads, head_dim, src_dtype,
+                                                cache_dtype, k_scale, v_scale, stream));
+}
+
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int cache_dtype, void *stream) {
+  if (num_pairs == 0 && k_cache && v_cache) return PA_OK;  // no-op; the pair array may be empty
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL_POINTER;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_BAD_SHAPE;
+  if (!known_dtype(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  const size_t block_bytes =
+      (size_t)block_size * num_kv_heads * head_dim * (size_t)elem_bytes(cache_dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  return status_of(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, block_bytes,
+                                          stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+"""Device decode against the oracle: ragged and edge context lengths, every
+supported element-type pair, head size and GQA group, single pass and split
+context, plus the properties that must hold exactly (invariance under block
+relabelling, aliased == private blocks, determinism, NaN-poisoned unused
+slots never read)."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_426_amd as pa
+import workloads as W
+from _helpers import assert_close, device_step, oracle_step, device_inputs, device_writes, \
+    device_decode
+
+pytestmark = pytest.mark.gpu
+
+EDGE_CTX = [1, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 256, 257, 511, 512, 513, 1023, 1025]
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3fn"),
+         ("f16", "fp8_e4m3fn")]
+
+
+def _check(wl, partition_size, what):
+    kc, vc, ref = oracle_step(wl)
+    d, out = device_step(wl, partition_size)
+    # the step's writes are bit-exact
+    assert np.array_equal(W.to_numpy(d["k_cache"]), kc), f"{what}: k_cache after writes"
+    assert np.array_equal(W.to_numpy(d["v_cache"]), vc), f"{what}: v_cache after writes"
+    return assert_close(W.widen_to_f64(out), ref, wl.q_dtype, what)
+
+
+def test_tiny_fp32_gqa2():
+    wl = W.build("tiny_fp32_gqa2")
+    for P in (0, 16, 32, 48):
+        err = _check(wl, P, f"tiny P={P}")
+        assert err <= 1e-5
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", PAIRS)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("P", [0, 16, 256])
+def test_edge_lengths(q_dtype, kv_dtype, d, P):
+    wl = W.custom(EDGE_CTX, 8, 2, d, q_dtype=q_dtype, kv_dtype=kv_dtype, seed=d + P)
+    _check(wl, P, f"{q_dtype}/{kv_dtype} d={d} P={P}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (12, 4), (16, 2), (16, 1), (32, 2)])
+@pytest.mark.parametrize("P", [0, 64])
+def test_gqa_groups(Hq, Hkv, P):
+    wl = W.custom([5, 100, 700], Hq, Hkv, 128, q_dtype="bf16", kv_dtype="bf16", seed=Hq * Hkv)
+    _check(wl, P, f"Hq={Hq} Hkv={Hkv} P={P}")
+
+
+def test_zero_context_gives_zeros():
+    wl = W.custom([0, 40, 0, 3], 4, 2, 64, q_dtype="bf16", kv_dtype="bf16", seed=1)
+    for P in (0, 16):
+        _check(wl, P, f"zero ctx P={P}")
+        d, out = device_step(wl, P)
+        o = W.widen_to_f64(out)
+        assert (o[0] == 0).all() and (o[2] == 0).all()
+
+
+@pytest.mark.parametrize("P", [0, 32])
+def test_poisoned_unused_slots_are_never_read(P):
+    """Unused block-table entries point at a NaN-filled block and the unused
+    tail of every last block is NaN: the output is finite and bitwise equal to
+    the clean run."""
+    wl = W.custom([17, 40, 1, 64], 8, 2, 128, q_dtype="bf16", kv_dtype="bf16", seed=5,
+                  extra_blocks=2)
+    kc, vc, _ = oracle_step(wl, decode=False)
+    clean = replace(wl, k_cache=kc, v_cache=vc, new_slots=None, new_key=None, new_value=None)
+    _, out_clean = device_step(clean, P)
+    nan16 = np.uint16(0x7FC0)
+    pk, pv = kc.copy(), vc.copy()
+    used = set()
+    for b, n in enumerate(wl.context_lens):
+        nblk = -(-int(n) // 16)
+        used.update(int(x) for x in wl.block_tables[b, :nblk])
+        last = wl.block_tables[b, nblk - 1]
+        tail = int(n) - (nblk - 1) * 16
+        pk[last, tail:] = nan16
+        pv[last, tail:] = nan16
+    poison = next(i for i in range(wl.num_blocks) if i not in used)
+    pk[poison] = nan16
+    pv[poison] = nan16
+    bt = wl.block_tables.copy()
+    for b, n in enumerate(wl.context_lens):
+        bt[b, -(-int(n) // 16):] = poison
+    dirty = replace(clean, k_cache=pk, v_cache=pv, block_tables=bt)
+    _, out_dirty = device_step(dirty, P)
+    o = W.widen_to_f64(out_dirty)
+    assert np.isfinite(o).all()
+    assert torch.equal(out_dirty, out_clean)
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_physical_relabelling_is_bitwise_invariant(P):
+    wl = W.custom([300, 17, 1000, 64], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", seed=9,
+                  extra_blocks=20)
+    _, a = device_step(wl, P)
+    _, b = device_step(W.permute_physical(wl, seed=10), P)
+    assert torch.equal(a, b)
+
+
+def test_aliased_blocks_equal_private_copies_bitwise():
+    wl = W.shared_prefix_cow_b64(groups=3, samples=4, prompt=96, parent_decoded=5, private=40)
+    kc, vc, ref = oracle_step(wl)
+    done = replace(wl, k_cache=kc, v_cache=vc, cow_pairs=np.zeros((0, 2), np.int64),
+                   hist_key=None, hist_value=None, hist_slots=None, hist_seq=None,
+                   new_key=None, new_value=None, new_slots=None)
+    private = W.unshare(done)
+    assert private.num_blocks > done.num_blocks
+    for P in (0, 32):
+        _, a = device_step(done, P)
+        _, b = device_step(private, P)
+        assert torch.equal(a, b)
+        assert_close(W.widen_to_f64(a), ref, "bf16", f"aliased P={P}")
+
+
+def test_copy_on_write_step_small():
+    """Fork, copy-on-write of the shared partial block, private writes, decode."""
+    wl = W.shared_prefix_cow_b64(groups=2, samples=4, prompt=64, parent_decoded=8, private=24)
+    assert len(wl.cow_pairs) == 6
+    for P in (0, 16):
+        _check(wl, P, f"cow P={P}")
+
+
+def test_deterministic():
+    wl = W.custom([2000, 333, 4096], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", seed=4)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    for P in (0, 256):
+        a = device_decode(wl, d, P)
+        b = device_decode(wl, d, P)
+        assert torch.equal(a, b)
+
+
+def test_partition_size_independence():
+    wl = W.custom([1, 700, 2500], 16, 4, 128, q_dtype="f32", kv_dtype="f32", seed=6)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    base = W.widen_to_f64(device_decode(wl, d, 0))
+    for P in (16, 48, 256, 1024, 4096):
+        other = W.widen_to_f64(device_decode(wl, d, P))
+        assert np.abs(other - base).max() <= 1e-5
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_split_partials_against_oracle(kv_dtype):
+    wl = W.custom([1, 95, 96, 97, 400], 8, 2, 128, q_dtype="bf16", kv_dtype=kv_dtype, seed=12)
+    P = 32
+    kc, vc, _ = oracle_step(wl, decode=False)
+    m, l, o = oracle.paged_decode_partials(wl.q, kc, vc, wl.block_tables, wl.context_lens,
+                                           wl.scale, P, wl.k_scale, wl.v_scale)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    tmp, mx, es = pa.decode_partials(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], P, scale=wl.scale, k_scale=wl.k_scale,
+                                     v_scale=wl.v_scale)
+    tmp, mx, es = (t.cpu().double().numpy() for t in (tmp, mx, es))
+    live = ~np.isnan(m)
+    assert np.abs(mx[live] - m[live]).max() <= 1e-4 * (1 + np.abs(m[live]).max())
+    assert np.allclose(es[live], l[live], rtol=1e-4, atol=1e-5)
+    assert np.allclose(tmp[live], o[live], rtol=1e-3, atol=1e-4)
+    out = pa.decode_reduce(*(torch.from_numpy(x).float().cuda() for x in (tmp, mx, es)),
+                           d["context_lens"], P, out_dtype=torch.float32)
+    ref = oracle.reduce_partials(m, l, o, wl.context_lens, P)
+    assert np.abs(out.cpu().double().numpy() - ref).max() <= 1e-4
+
+
+def test_fp8_decode_widening_covers_every_code():
+    """Context of one token: the output is that token's V row times v_scale,
+    exactly representable in bf16; V holds every finite E4M3FN code."""
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[np.isfinite(oracle.e4m3fn_decode(codes))]      # 254 codes
+    row = np.resize(finite, 2 * 128).reshape(2, 128)               # two KV heads
+    kc = np.zeros((2, 16, 2, 128), np.uint8)
+    vc = np.zeros((2, 16, 2, 128), np.uint8)
+    vc[1, 0] = row
+    q = W.configs.normal(np.random.default_rng(0), (1, 4, 128), "bf16")
+    bt = np.asarray([[1]], np.int32)
+    cl = np.asarray([1], np.int32)
+    out = pa.decode(W.to_device(q), W.to_device(kc), W.to_device(vc), W.to_device(bt),
+                    W.to_device(cl), k_scale=1.0, v_scale=1.0)
+    got = W.widen_to_f64(out)[0]
+    expect = oracle.e4m3fn_decode(row)
+    for h in range(4):
+        assert np.array_equal(got[h], expect[h // 2])

@@ -5,6 +5,7 @@ attention or cache-write arithmetic.
 """
 
 from .blockpool import BlockPool, PoolExhausted, Sequence
+from .torch_io import to_device, to_numpy, widen_to_f64
 from .configs import (
     BUILDERS,
     ELEM_BYTES,
@@ -36,4 +37,7 @@ __all__ = [
     "tiny_fp32_gqa2",
     "permute_physical",
     "unshare",
+    "to_device",
+    "to_numpy",
+    "widen_to_f64",
 ]

@@ -73,6 +73,7 @@ class Workload:
     hist_key: Optional[np.ndarray] = None     # [Nh, Hkv, d] (q dtype)
     hist_value: Optional[np.ndarray] = None
     hist_slots: Optional[np.ndarray] = None   # [Nh] int64
+    hist_seq: Optional[np.ndarray] = None     # [Nh] int32: the sequence each history token belongs to
     new_key: Optional[np.ndarray] = None      # [B, Hkv, d] (q dtype)
     new_value: Optional[np.ndarray] = None
     new_slots: Optional[np.ndarray] = None    # [B] int64
@@ -220,18 +221,22 @@ def shared_prefix_cow_b64(seed: int = 4, partition_size: int = 256, groups: int 
         for p in parents:
             seqs += [p] + [pool.fork(p) for _ in range(samples - 1)]
         shared_ratio_after_fork = pool.shared_ratio()
-        cow, hist, new = [], [], []
+        cow, hist, new, owner = [], [], [], []
         for step in range(private):
-            for s in seqs:
+            for i, s in enumerate(seqs):
                 slot, pair = pool.append_slot(s)
                 if pair is not None:
                     cow.append(pair)
-                (hist if step < private - 1 else new).append(slot)
-        return pool, seqs, cow, hist, new, shared_ratio_after_fork
+                if step < private - 1:
+                    hist.append(slot)
+                    owner.append(i)
+                else:
+                    new.append(slot)
+        return pool, seqs, cow, hist, new, owner, shared_ratio_after_fork
 
     used = simulate(1 << 20, None)[0].blocks_in_use()
     nb = math.ceil(1.1 * used)
-    pool, seqs, cow, hist, new, ratio_fork = simulate(nb, rng.permutation(nb))
+    pool, seqs, cow, hist, new, owner, ratio_fork = simulate(nb, rng.permutation(nb))
     B = len(seqs)
     ctx = np.asarray([s.length for s in seqs], dtype=np.int32)
     mbs = max(len(s.block_table) for s in seqs)
@@ -250,7 +255,7 @@ def shared_prefix_cow_b64(seed: int = 4, partition_size: int = 256, groups: int 
         context_lens=ctx, scale=float(np.float32(1.0 / math.sqrt(d))),
         cow_pairs=np.asarray(cow, dtype=np.int64).reshape(-1, 2),
         hist_key=hist_key, hist_value=hist_value,
-        hist_slots=np.asarray(hist, dtype=np.int64),
+        hist_slots=np.asarray(hist, dtype=np.int64), hist_seq=np.asarray(owner, dtype=np.int32),
         new_key=new_key, new_value=new_value, new_slots=np.asarray(new, dtype=np.int64),
         partition_size=partition_size,
         info={"blocks_used": pool.blocks_in_use(), "shared_ratio": pool.shared_ratio(),
@@ -280,6 +285,7 @@ def long_ctx_fp8_b8(seed: int = 5, partition_size: int = 512, batch: int = 8,
     hist_slots = np.concatenate([
         _slots_of_positions(s.block_table, np.arange(int(n) - 1), bs)
         for s, n in zip(seqs, ctx)])
+    hist_seq = np.repeat(np.arange(batch, dtype=np.int32), ctx - 1)
     q = normal(rng, (batch, Hq, d), "bf16")
     hist_key = normal(rng, (len(hist_slots), Hkv, d), "bf16")
     hist_value = normal(rng, (len(hist_slots), Hkv, d), "bf16")
@@ -298,7 +304,7 @@ def long_ctx_fp8_b8(seed: int = 5, partition_size: int = 512, batch: int = 8,
         block_tables=_tables(seqs, 32768 // bs), context_lens=ctx,
         scale=float(np.float32(1.0 / math.sqrt(d))),
         k_scale=amax_scale(hist_key, new_key), v_scale=amax_scale(hist_value, new_value),
-        hist_key=hist_key, hist_value=hist_value, hist_slots=hist_slots,
+        hist_key=hist_key, hist_value=hist_value, hist_slots=hist_slots, hist_seq=hist_seq,
         new_key=new_key, new_value=new_value, new_slots=new_slots,
         partition_size=partition_size,
         info={"blocks_used": pool.blocks_in_use(), "shared_ratio": pool.shared_ratio()},
@@ -356,12 +362,14 @@ def custom(ctx_lens, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16", bs=16, seed=0,
         hist_slots = np.concatenate([
             _slots_of_positions(s.block_table, np.arange(int(n) - 1), bs)
             for s, n in zip(seqs, ctx_lens) if n > 1] or [np.zeros(0, np.int64)])
+        hist_seq = np.repeat(np.arange(len(ctx_lens), dtype=np.int32),
+                             np.maximum(ctx_lens.astype(np.int64) - 1, 0))
         hist_key = normal(rng, (len(hist_slots), Hkv, d), q_dtype)
         hist_value = normal(rng, (len(hist_slots), Hkv, d), q_dtype)
     else:
         k_cache = normal(rng, (nb, bs, Hkv, d), kv_dtype)
         v_cache = normal(rng, (nb, bs, Hkv, d), kv_dtype)
-        hist_slots = hist_key = hist_value = None
+        hist_slots = hist_key = hist_value = hist_seq = None
     q = normal(rng, (B, Hq, d), q_dtype)
     new_key = normal(rng, (B, Hkv, d), q_dtype)
     new_value = normal(rng, (B, Hkv, d), q_dtype)
@@ -370,7 +378,8 @@ def custom(ctx_lens, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16", bs=16, seed=0,
         num_blocks=nb, q_dtype=q_dtype, kv_dtype=kv_dtype, q=q, k_cache=k_cache,
         v_cache=v_cache, block_tables=_tables(seqs, mbs), context_lens=ctx_lens,
         scale=float(np.float32(1.0 / math.sqrt(d))), hist_key=hist_key,
-        hist_value=hist_value, hist_slots=hist_slots, new_key=new_key, new_value=new_value,
+        hist_value=hist_value, hist_slots=hist_slots, hist_seq=hist_seq, new_key=new_key,
+        new_value=new_value,
         new_slots=np.asarray(slots, dtype=np.int64), partition_size=partition_size,
         info={"blocks_used": pool.blocks_in_use()},
     )
@@ -438,4 +447,4 @@ def unshare(wl: Workload) -> Workload:
     v = np.concatenate([wl.v_cache, np.stack(extra_v)]) if extra_v else wl.v_cache.copy()
     return replace(wl, k_cache=k, v_cache=v, block_tables=tables, num_blocks=nb,
                    cow_pairs=np.zeros((0, 2), np.int64), hist_key=None, hist_value=None,
-                   hist_slots=None, new_key=None, new_value=None, new_slots=None)
+                   hist_slots=None, hist_seq=None, new_key=None, new_value=None, new_slots=None)
