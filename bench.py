@@ -1,0 +1,401 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--partition-size P] [--layers L] [--no-cpu-baseline]
+
+One step is one pass of the whole decode hot path over one batch of synthetic
+input, on one attention layer: the copy-on-write block copies the workload
+needs (none for most), the slot write of every sequence's new K/V token, and
+paged decode (split-context partials plus the cross-partition merge when the
+partition size is non-zero). Steps rotate over L layer caches that share one
+block table -- as real decode does layer by layer -- so that consecutive
+steps read K/V from HBM rather than from the 256 MB last-level cache.
+
+Inputs are resident in HBM before the timed region starts. Rank 0 prints one
+JSON line:
+
+  value      KV tokens attended per second (sum of context lengths / step time)
+  gbps       algorithmic HBM GB/s of the step (every attended K/V byte once,
+             plus q, out and the block-table entries read)
+  roofline   the dominant kernel (the decode kernel) timed alone with HIP
+             events on the stream it is launched on: algorithmic bytes per
+             launch / average launch time, against 8 TB/s
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same
+             workload, on this host's cores (a reported baseline only)
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+DEFAULT_WORKLOAD = "llama3_8b_b32"
+DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn"}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1}
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_426_amd", "csrc", "pa_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3_8b_b32_traffic.md")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per split-context partition (0 = single pass); "
+                         "default: the workload's own launch configuration")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="layer caches rotated over (defeats the last-level cache)")
+    ap.add_argument("--roofline-launches", type=int, default=400)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (a known byte count for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    return ap.parse_args(argv)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte counts
+# ---------------------------------------------------------------------------
+
+def decode_bytes(wl):
+    """Algorithmic HBM bytes of one decode: every attended token's K and V row
+    of every KV head once, q read once, out written once, and the block-table
+    entries of the blocks attended."""
+    kv_tok = 2 * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+    q_bytes = wl.q.size * ELEM_BYTES[wl.q_dtype]
+    tables = sum(-(-int(n) // wl.block_size) for n in wl.context_lens) * 4
+    kv = wl.tokens_attended * kv_tok
+    return {"kv": kv, "kv_per_token": kv_tok, "q": q_bytes, "out": q_bytes, "tables": tables,
+            "ctx_lens": 4 * wl.num_seqs,
+            "total": kv + 2 * q_bytes + tables + 4 * wl.num_seqs}
+
+
+def unique_kv_bytes(wl):
+    """K/V bytes of the distinct (block, offset) slots attended: the minimum a
+    decode must read when blocks are shared between sequences."""
+    import numpy as np
+
+    bs = wl.block_size
+    slots = set()
+    for b in range(wl.num_seqs):
+        n = int(wl.context_lens[b])
+        ids = np.asarray(wl.block_tables[b, : -(-n // bs)], dtype=np.int64)
+        pos = np.arange(n)
+        slots.update((ids[pos // bs] * bs + pos % bs).tolist())
+    return len(slots) * 2 * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+
+
+def write_bytes(wl):
+    """Slot write: read each new token's K/V rows, write them to the cache."""
+    if wl.new_slots is None:
+        return 0
+    n = int((wl.new_slots >= 0).sum())
+    row = wl.num_kv_heads * wl.head_dim
+    return n * 2 * row * (ELEM_BYTES[wl.q_dtype] + ELEM_BYTES[wl.kv_dtype]) + 8 * len(wl.new_slots)
+
+
+def copy_bytes(wl):
+    blk = wl.block_size * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+    return len(wl.cow_pairs) * 2 * 2 * blk
+
+
+# ---------------------------------------------------------------------------
+# traffic measured by rocprofv3 counters (committed summary)
+# ---------------------------------------------------------------------------
+
+def decode_source_hash():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload, partition_size):
+    """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
+    summary, or None when there is none for this workload / partition size or
+    the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    try:
+        if fields.get("workload") != workload or int(fields["partition_size"]) != partition_size:
+            return None
+        if fields.get("decode_source_sha256") != decode_source_hash():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands (slot write of the new tokens, then decode) on
+    whole sequences of the same workload, one sequence at a time, until the
+    time budget is spent. Returns KV tokens attended per second."""
+    import numpy as np
+
+    import oracle
+
+    kc, vc = wl.k_cache, wl.v_cache
+    done_tokens, done_seqs, t_used = 0, 0, 0.0
+    order = [int(b) for b in np.random.default_rng(0).permutation(wl.num_seqs)]
+    while t_used < budget_s:
+        b = order[done_seqs % len(order)]
+        t0 = time.perf_counter()
+        if wl.new_slots is not None and wl.new_slots[b] >= 0:
+            oracle.reshape_and_cache(wl.new_key[b:b + 1], wl.new_value[b:b + 1], kc, vc,
+                                     wl.new_slots[b:b + 1], wl.k_scale, wl.v_scale)
+        oracle.paged_decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale,
+                            wl.k_scale, wl.v_scale, seqs=[b])
+        t_used += time.perf_counter() - t0
+        done_tokens += int(wl.context_lens[b])
+        done_seqs += 1
+    try:  # BLAS threads actually in use, read after the oracle has run
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+    except Exception:  # noqa: BLE001
+        info = []
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": done_tokens / t_used,
+        "unit": "KV tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{done_seqs} sequence decodes ({done_seqs / wl.num_seqs:.2f} passes over "
+                   f"the {wl.num_seqs} sequences) of {wl.name} "
+                   f"({done_tokens} KV tokens attended, slot write + float64 decode), "
+                   f"{t_used:.1f} s wall-clock; python loop with numpy BLAS on "
+                   f"{threads} thread(s), {len(os.sched_getaffinity(0))} host cores visible"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: paged decode here runs on a single MI355X "
+              f"with no sharding or collectives (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_426_amd as pa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    kw = {} if args.partition_size is None else {"partition_size": args.partition_size}
+    wl = W.build(args.workload, **kw)
+    P = wl.partition_size
+    log(f"workload {wl.name}: B={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"d={wl.head_dim} kv={wl.kv_dtype} P={P} tokens={wl.tokens_attended} "
+        f"pool={wl.num_blocks} blocks (built in {time.perf_counter() - t0:.1f} s)")
+
+    # device inputs; the step's history writes (fp8 fill, private tokens) are
+    # applied once, before timing, to every layer cache
+    t = lambda a: W.to_device(a, dev)  # noqa: E731
+    q = t(wl.q)
+    bt = t(wl.block_tables)
+    cl = t(wl.context_lens)
+    cow = t(wl.cow_pairs)
+    new_k = t(wl.new_key) if wl.new_key is not None else None
+    new_v = t(wl.new_value) if wl.new_value is not None else None
+    new_s = t(wl.new_slots) if wl.new_slots is not None else None
+    k0, v0 = t(wl.k_cache), t(wl.v_cache)
+    if wl.hist_slots is not None and len(wl.hist_slots):
+        pa.copy_blocks(k0, v0, cow)
+        pa.reshape_and_cache(t(wl.hist_key), t(wl.hist_value), k0, v0, t(wl.hist_slots),
+                             wl.k_scale, wl.v_scale)
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.layers - 1)]
+    out = torch.empty_like(q)
+    MBS = wl.max_blocks_per_seq
+    NP = pa.num_partitions(MBS, wl.block_size, P) if P else 0
+    ws = None
+    if P:
+        ws = torch.empty(pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
+                                                  MBS, wl.block_size, P),
+                         dtype=torch.uint8, device=dev)
+    has_cow = len(wl.cow_pairs) > 0
+    torch.cuda.synchronize()
+
+    def step(i):
+        kc, vc = layers[i % len(layers)]
+        if has_cow:
+            pa.copy_blocks(kc, vc, cow)
+        if new_s is not None:
+            pa.reshape_and_cache(new_k, new_v, kc, vc, new_s, wl.k_scale, wl.v_scale)
+        pa.decode(q, kc, vc, bt, cl, scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                  partition_size=P, out=out, workspace=ws)
+
+    # --- whole-step throughput ---------------------------------------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.2f} us/step on events, "
+        f"{wall / args.steps * 1e6:.2f} us/step wall-clock")
+
+    # --- the dominant kernel alone: per-launch HIP events on its stream ------
+    # With a partition size the decode kernel writes split partials (the merge
+    # is a separate, small kernel); without one it writes the output directly.
+    n_launch = args.roofline_launches
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    if P:
+        nbh = wl.num_seqs * wl.num_q_heads * NP
+        flat = ws.view(torch.float32)
+        tmp_out = flat[: nbh * wl.head_dim].view(wl.num_seqs, wl.num_q_heads, NP, wl.head_dim)
+        max_logits = flat[nbh * wl.head_dim: nbh * (wl.head_dim + 1)].view(
+            wl.num_seqs, wl.num_q_heads, NP)
+        exp_sums = flat[nbh * (wl.head_dim + 1): nbh * (wl.head_dim + 2)].view(
+            wl.num_seqs, wl.num_q_heads, NP)
+
+        def kernel(i):
+            kc, vc = layers[i % len(layers)]
+            pa.decode_partials(q, kc, vc, bt, cl, P, scale=wl.scale, k_scale=wl.k_scale,
+                               v_scale=wl.v_scale, tmp_out=tmp_out, max_logits=max_logits,
+                               exp_sums=exp_sums)
+    else:
+        def kernel(i):
+            kc, vc = layers[i % len(layers)]
+            pa.decode(q, kc, vc, bt, cl, scale=wl.scale, k_scale=wl.k_scale,
+                      v_scale=wl.v_scale, partition_size=0, out=out)
+    for i in range(10):
+        kernel(i)
+    torch.cuda.synchronize()
+    for i in range(n_launch):
+        starts[i].record(stream)
+        kernel(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    kern_med_s = sorted(kern_ms)[len(kern_ms) // 2] / 1e3
+
+    # --- optional copy calibration for counter scaling ----------------------
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: one 1 GiB device-to-device copy (1 GiB read + 1 GiB written)")
+        del src, dst
+
+    # --- bytes and the JSON line ---------------------------------------------
+    db = decode_bytes(wl)
+    kernel_alg = db["kv"] + db["q"] + db["tables"] + db["ctx_lens"]
+    if not P:
+        kernel_alg += db["out"]
+    step_alg = db["total"] + write_bytes(wl) + copy_bytes(wl)
+    tokens = wl.tokens_attended
+    step_s = ms_per_step / 1e3
+    achieved = kernel_alg / kern_avg_s / 1e9
+    result = {
+        "metric": "paged decode: KV tokens attended/s and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": tokens / step_s,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[wl.kv_dtype] if wl.kv_dtype == wl.q_dtype
+        else f"{wl.q_dtype}/{wl.kv_dtype}",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": wl.num_seqs,
+            "context_tokens_total": tokens,
+            "context_len_min": int(wl.context_lens.min()),
+            "context_len_max": int(wl.context_lens.max()),
+            "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim,
+            "block_size": wl.block_size,
+            "num_blocks": wl.num_blocks,
+            "q_dtype": wl.q_dtype,
+            "kv_dtype": wl.kv_dtype,
+            "partition_size": P,
+            "layers_rotated": args.layers,
+            "step": ("copy_blocks + " if has_cow else "") +
+                    "reshape_and_cache(new tokens) + decode" +
+                    (" (partials + merge)" if P else " (single pass)"),
+        },
+        "gbps": step_alg / step_s / 1e9,
+        "hbm_frac": step_alg / step_s / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_alg,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": committed_traffic(wl.name, P),
+            "kernel": "decode_kernel" + (" (split partials)" if P else " (single pass)"),
+            "kernel_avg_us": kern_avg_s * 1e6,
+            "kernel_median_us": kern_med_s * 1e6,
+            "algorithmic_bytes_per_launch": kernel_alg,
+            "bytes_per_unit": db["kv_per_token"],
+            "units_per_launch": tokens,
+        },
+    }
+    if "distinct_blocks" in wl.info:
+        ub = unique_kv_bytes(wl)
+        result["unique_kv_bytes"] = ub
+        result["unique_kv_gbps_kernel"] = ub / kern_avg_s / 1e9
+        result["shared_ratio"] = wl.info.get("shared_ratio")
+
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
