@@ -238,7 +238,7 @@ def main(argv=None):
     layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.layers - 1)]
     out = torch.empty_like(q)
     MBS = wl.max_blocks_per_seq
-    NP = pa.num_partitions(MBS, wl.block_size, P) if P else 0
+    NP = pa.num_partitions(MBS, wl.block_size, P) if P > 0 else 0
     ws = None
     if P:
         ws = torch.empty(pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
@@ -281,7 +281,7 @@ def main(argv=None):
     n_launch = args.roofline_launches
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
-    if P:
+    if P > 0:
         nbh = wl.num_seqs * wl.num_q_heads * NP
         flat = ws.view(torch.float32)
         tmp_out = flat[: nbh * wl.head_dim].view(wl.num_seqs, wl.num_q_heads, NP, wl.head_dim)
@@ -289,10 +289,22 @@ def main(argv=None):
             wl.num_seqs, wl.num_q_heads, NP)
         exp_sums = flat[nbh * (wl.head_dim + 1): nbh * (wl.head_dim + 2)].view(
             wl.num_seqs, wl.num_q_heads, NP)
-
+        split_arg = P
+    elif P < 0:
+        # the balanced split's partial kernel alone, with the share count the
+        # automatic choice resolves to
+        S = pa.decode_balanced_splits(wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                      q.dtype, layers[0][0].dtype) if P == -1 else -P
+        npc = S + wl.num_seqs
+        tmp_out = torch.empty((wl.num_q_heads, npc, wl.head_dim), dtype=torch.float32, device=dev)
+        max_logits = torch.empty((wl.num_q_heads, npc), dtype=torch.float32, device=dev)
+        exp_sums = torch.empty((wl.num_q_heads, npc), dtype=torch.float32, device=dev)
+        split_arg = -S
+        log(f"balanced split: {S} shares")
+    if P:
         def kernel(i):
             kc, vc = layers[i % len(layers)]
-            pa.decode_partials(q, kc, vc, bt, cl, P, scale=wl.scale, k_scale=wl.k_scale,
+            pa.decode_partials(q, kc, vc, bt, cl, split_arg, scale=wl.scale, k_scale=wl.k_scale,
                                v_scale=wl.v_scale, tmp_out=tmp_out, max_logits=max_logits,
                                exp_sums=exp_sums)
     else:

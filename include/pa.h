@@ -26,8 +26,9 @@
  *   - Every data pointer is a DEVICE pointer to contiguous row-major memory
  *     owned by the caller. The library borrows it for the work it enqueues
  *     and keeps no reference afterwards; the caller keeps it alive until the
- *     stream has passed that work. The library allocates no memory, holds no
- *     global state and is reentrant.
+ *     stream has passed that work. The library allocates no memory and is
+ *     reentrant; its only process-wide data is a cache of device properties
+ *     (compute-unit count, kernel occupancy) behind a mutex.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default
  *     stream. All work is enqueued asynchronously on it.
  *   - Cache layout: k_cache and v_cache are [num_blocks, block_size,
@@ -80,16 +81,51 @@ const char *pa_status_string(int status);
 int pa_version(void);
 
 /*
- * Number of partitions a split-context decode uses for a block table of
+ * Context splitting. Every decode entry point takes a partition_size:
+ *
+ *   0      single pass: one workgroup reads a sequence's whole context.
+ *   P > 0  fixed split: partition p of sequence b covers logical tokens
+ *          [p*P, min((p+1)*P, n)); P is a multiple of block_size.
+ *   -S     balanced split with S >= 2 shares: the cache blocks of all
+ *          sequences, taken end to end in sequence order (ceil(n_b / 16)
+ *          blocks for sequence b, T in total), are cut into S shares, share
+ *          s being blocks [floor(s*T/S), floor((s+1)*T/S)) (S is first
+ *          clamped to T). Each piece = (share, sequence) intersection is one
+ *          partial; every share holds the same number of blocks, so the work
+ *          is even whatever the length mix. At most 1024 sequences.
+ *   -1     (pa_decode only) balanced split with the share count that fills
+ *          every compute unit of the current device once:
+ *          pa_decode_balanced_splits(...).
+ *
+ * Splits change only the order of the floating-point reductions, never the
+ * mathematical result. The balanced split of one sequence depends on the
+ * other sequences' lengths (through T).
+ */
+
+/*
+ * Number of partitions a fixed split uses for a block table of
  * max_blocks_per_seq entries: ceil(max_blocks_per_seq * block_size /
  * partition_size). Returns 0 for partition_size <= 0.
  */
 int pa_num_partitions(int max_blocks_per_seq, int block_size, int partition_size);
 
 /*
- * Bytes of device workspace pa_decode needs: 0 when partition_size == 0
- * (single pass), otherwise the split partials of pa_decode_partials:
- * num_seqs * num_q_heads * NP * (head_dim + 2) * 4, NP as above.
+ * Share count of the automatic balanced split (partition_size = -1) on the
+ * current device for this head and type configuration: the number of
+ * workgroups that fill every compute unit once at the decode kernel's
+ * occupancy, divided by the workgroups per share (num_kv_heads * query-head
+ * runs), at least 2 and at most 2048. Returns 0 for an unsupported
+ * configuration. Queries the device (HIP runtime) on first use.
+ */
+int pa_decode_balanced_splits(int num_q_heads, int num_kv_heads, int head_dim, int q_dtype,
+                              int kv_dtype);
+
+/*
+ * Bytes of device workspace pa_decode needs:
+ *   partition_size == 0: 0;
+ *   P > 0:  num_seqs * num_q_heads * NP * (head_dim + 2) * 4, NP as above;
+ *   -S:     num_q_heads * (S + num_seqs) * (head_dim + 2) * 4, with S = 2048
+ *           (the largest automatic choice) for partition_size = -1.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                 int max_blocks_per_seq, int block_size,
@@ -122,12 +158,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *                 ceil(n / block_size) entries of row b are read.
  *   context_lens  [num_seqs] int32, each in [0, max_blocks_per_seq*block_size].
  *   scale         softmax scale, normally 1/sqrt(head_dim).
- *   partition_size 0: one pass over the whole context per (sequence, KV
- *                 head). > 0 (a multiple of block_size): split-context
- *                 decode -- pa_decode_partials into `workspace`, then
- *                 pa_decode_reduce into `out` (same stream).
+ *   partition_size see "Context splitting" above. A split decode runs the
+ *                 partial kernel into `workspace` (a sequence that falls in
+ *                 one piece is written to `out` directly), then the merge
+ *                 kernel into `out`, on the same stream.
  *   workspace     device buffer of at least pa_decode_workspace_size(...)
- *                 bytes when partition_size > 0 (may be NULL otherwise). Its
+ *                 bytes when partition_size != 0 (may be NULL otherwise). Its
  *                 contents on entry do not matter; one call at a time may use
  *                 a given workspace.
  */
@@ -140,26 +176,30 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     void *stream);
 
 /*
- * pa_decode_partials -- the per-partition half of split-context decode.
+ * pa_decode_partials -- the per-piece half of split-context decode.
  *
- * Partition p of sequence b covers logical tokens [p*P, min((p+1)*P, n)),
- * P = partition_size (a multiple of block_size), n = context_lens[b]. For
- * each (b, h, p) with p < ceil(n / P) it writes, in float32,
+ * For each piece (a fixed partition p of sequence b, or a balanced-split
+ * piece: share s intersected with sequence b) over logical tokens J and each
+ * query head h, it writes in float32
  *
- *   max_logits[b, h, p] = m = max_j s_j                     (s_j as in pa_decode)
- *   exp_sums[b, h, p]   = l = sum_j exp(s_j - m)
- *   tmp_out[b, h, p, :] =     sum_j exp(s_j - m) * v_scale * V[j] / l
+ *   max_logits = m = max_{j in J} s_j                       (s_j as in pa_decode)
+ *   exp_sums   = l = sum_{j in J} exp(s_j - m)
+ *   tmp_out    =     sum_{j in J} exp(s_j - m) * v_scale * V[j] / l
  *
- * Entries with p >= ceil(n / P) are not written. Merging the partials of a
- * sequence (pa_decode_reduce) gives the same attention as pa_decode; the
- * partials of one sequence may also be produced on different devices and
- * merged afterwards.
- *
- *   tmp_out      [num_seqs, num_q_heads, max_partitions, head_dim] float32
- *   max_logits   [num_seqs, num_q_heads, max_partitions] float32
- *   exp_sums     [num_seqs, num_q_heads, max_partitions] float32
+ * Fixed split (partition_size = P > 0): entry [b, h, p] for p < ceil(n / P);
+ *   tmp_out [num_seqs, num_q_heads, max_partitions, head_dim],
+ *   max_logits / exp_sums [num_seqs, num_q_heads, max_partitions],
  *   max_partitions >= pa_num_partitions(max_blocks_per_seq, block_size, P).
- * Other arguments as in pa_decode.
+ * Balanced split (partition_size = -S, S >= 2; -1 is refused here: resolve
+ * the automatic count with pa_decode_balanced_splits first): entry
+ * [h, s + b] for each non-empty piece (s, b);
+ *   tmp_out [num_q_heads, max_partitions, head_dim],
+ *   max_logits / exp_sums [num_q_heads, max_partitions],
+ *   max_partitions >= S + num_seqs.
+ * Other entries are not written. Merging the pieces of a sequence
+ * (pa_decode_reduce) gives the same attention as pa_decode; the pieces of
+ * one sequence may also be produced on different devices and merged
+ * afterwards. Other arguments as in pa_decode.
  */
 pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
                              int max_partitions, const void *q, const void *k_cache,
@@ -172,13 +212,16 @@ pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
 /*
  * pa_decode_reduce -- merge split-context partials into the decode output.
  *
- * For each (b, h), over the first ceil(n / P) partitions: M = max_p m_p,
- * w_p = l_p * exp(m_p - M), out[b, h] = sum_p w_p * tmp_out[b, h, p] /
- * sum_p w_p, rounded to out_dtype (round to nearest even). n == 0 gives 0.
+ * For each (b, h), over the pieces of sequence b (fixed split: the first
+ * ceil(n / P) partitions; balanced split: the shares s0..s1 that hold its
+ * blocks): M = max_p m_p, w_p = l_p * exp(m_p - M), out[b, h] =
+ * sum_p w_p * tmp_out[p] / sum_p w_p, rounded to out_dtype (round to nearest
+ * even). n == 0 gives 0.
  *
  *   out          [num_seqs, num_q_heads, head_dim], out_dtype (f32, f16, bf16)
- *   tmp_out, max_logits, exp_sums, max_partitions: as written by
- *                pa_decode_partials with the same partition_size.
+ *   tmp_out, max_logits, exp_sums, max_partitions, partition_size: as given
+ *                to pa_decode_partials (same context_lens).
+ *   head_dim     64 or 128.
  */
 pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_logits,
                            const float *exp_sums, const int32_t *context_lens,

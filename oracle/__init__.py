@@ -44,6 +44,9 @@ from .attention import (
     paged_decode_partials,
     reduce_partials,
     gather_logical_kv,
+    balanced_pieces,
+    paged_decode_pieces,
+    reduce_pieces,
 )
 from .cache_ops import reshape_and_cache, copy_blocks
 from . import sizes
@@ -57,6 +60,9 @@ __all__ = [
     "paged_decode_partials",
     "reduce_partials",
     "gather_logical_kv",
+    "balanced_pieces",
+    "paged_decode_pieces",
+    "reduce_pieces",
     "reshape_and_cache",
     "copy_blocks",
     "sizes",

@@ -162,6 +162,85 @@ def reduce_partials(m, l, o, context_lens, partition_size):
     return out
 
 
+def balanced_pieces(context_lens, block_size, num_splits):
+    """The pieces of the balanced split, as the library's header defines it.
+
+    The blocks of all sequences are taken end to end in sequence order
+    (ceil(n_b / bs) blocks for sequence b, T in all); with S' = min(S, T),
+    share s holds blocks [floor(s T / S'), floor((s+1) T / S')). A piece is
+    the intersection of a share with one sequence. Returns a list of
+    (s, b, first_block, end_block), block indices local to sequence b, in
+    (share, sequence) order. The split is the library's own work division
+    (the pages do not describe one); merging the pieces gives the dense
+    result whatever the split.
+    """
+    nblk = [-(-max(int(n), 0) // block_size) for n in context_lens]
+    T = sum(nblk)
+    if T == 0:
+        return []
+    S = min(int(num_splits), T)
+    starts = np.concatenate([[0], np.cumsum(nblk)])
+    pieces = []
+    for s in range(S):
+        lo, hi = s * T // S, (s + 1) * T // S
+        for b in range(len(nblk)):
+            a, z = max(lo, int(starts[b])), min(hi, int(starts[b + 1]))
+            if a < z:
+                pieces.append((s, b, a - int(starts[b]), z - int(starts[b])))
+    return pieces
+
+
+def paged_decode_pieces(q, k_cache, v_cache, block_tables, context_lens, scale, pieces,
+                        k_scale=1.0, v_scale=1.0):
+    """(m, l, o~) of each piece (s, b, first_block, end_block) for every query
+    head: the softmax statistics of the piece's own tokens
+    [first_block * bs, min(end_block * bs, n)), as in paged_decode_partials.
+    Shapes: m, l [len(pieces), Hq]; o~ [len(pieces), Hq, d]."""
+    q64 = to_f64(q)
+    B, Hq, d = q64.shape
+    bs = k_cache.shape[1]
+    group = Hq // k_cache.shape[2]
+    scale64 = float(np.float32(scale))
+    ks = float(np.float32(k_scale))
+    vs = float(np.float32(v_scale))
+    m = np.zeros((len(pieces), Hq))
+    l = np.zeros((len(pieces), Hq))
+    o = np.zeros((len(pieces), Hq, d))
+    for i, (_, b, fb, eb) in enumerate(pieces):
+        n = int(context_lens[b])
+        nblk = -(-n // bs)
+        ids = np.asarray(block_tables[b][:nblk], dtype=np.int64)
+        K = gather_logical_kv(to_f64(k_cache[ids]), np.arange(nblk), n) * ks
+        V = gather_logical_kv(to_f64(v_cache[ids]), np.arange(nblk), n) * vs
+        lo, hi = fb * bs, min(eb * bs, n)
+        for h in range(Hq):
+            g = h // group
+            sc = (K[lo:hi, g, :] @ q64[b, h]) * scale64
+            mp = sc.max()
+            e = np.exp(sc - mp)
+            m[i, h] = mp
+            l[i, h] = e.sum()
+            o[i, h] = (e @ V[lo:hi, g, :]) / e.sum()
+    return m, l, o
+
+
+def reduce_pieces(m, l, o, pieces, num_seqs):
+    """Merge pieces per sequence exactly as reduce_partials merges partitions:
+    float64 [B, Hq, d]; a sequence with no piece gives zeros."""
+    Hq, d = o.shape[1:]
+    out = np.zeros((num_seqs, Hq, d))
+    for b in range(num_seqs):
+        idx = [i for i, pc in enumerate(pieces) if pc[1] == b]
+        if not idx:
+            continue
+        for h in range(Hq):
+            mp = m[idx, h]
+            M = mp.max()
+            w = l[idx, h] * np.exp(mp - M)
+            out[b, h] = (w @ o[idx, h]) / w.sum()
+    return out
+
+
 def default_scale(head_dim: int) -> float:
     """The softmax scale 1/sqrt(d_k) of the attention formula, as float32."""
     return float(np.float32(1.0 / math.sqrt(head_dim)))

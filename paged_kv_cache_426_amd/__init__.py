@@ -20,8 +20,12 @@ __all__ = [
     "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN",
     "PaError", "lib", "library_path", "dtype_code",
     "decode", "decode_partials", "decode_reduce", "decode_workspace_size",
-    "num_partitions", "reshape_and_cache", "copy_blocks",
+    "num_partitions", "decode_balanced_splits", "reshape_and_cache", "copy_blocks",
+    "PARTITION_AUTO",
 ]
+
+# partition_size of the balanced split with the automatic share count
+PARTITION_AUTO = -1
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2, 3
 
@@ -63,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.pa_version.restype = i32
         L.pa_num_partitions.restype = i32
         L.pa_num_partitions.argtypes = [i32, i32, i32]
+        L.pa_decode_balanced_splits.restype = i32
+        L.pa_decode_balanced_splits.argtypes = [i32] * 5
         L.pa_decode_workspace_size.restype = sz
         L.pa_decode_workspace_size.argtypes = [i32] * 6
         L.pa_decode.restype = i32
@@ -130,6 +136,14 @@ def num_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int
     return lib().pa_num_partitions(max_blocks_per_seq, block_size, partition_size)
 
 
+def decode_balanced_splits(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           q_dtype: torch.dtype, kv_dtype: torch.dtype) -> int:
+    """Share count of the automatic balanced split on the current device
+    (C: pa_decode_balanced_splits); 0 for an unsupported configuration."""
+    return lib().pa_decode_balanced_splits(num_q_heads, num_kv_heads, head_dim,
+                                           _DTYPES[q_dtype], _DTYPES[kv_dtype])
+
+
 def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
                           max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
     return lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
@@ -178,25 +192,31 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, partition_s
                     scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0,
                     tmp_out=None, max_logits=None, exp_sums=None
                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Split-context partials (C: pa_decode_partials): returns
-    (tmp_out [B, Hq, NP, d], max_logits [B, Hq, NP], exp_sums [B, Hq, NP]), float32."""
+    """Split-context partials (C: pa_decode_partials), float32.
+
+    Fixed split (partition_size > 0): tmp_out [B, Hq, NP, d], max_logits and
+    exp_sums [B, Hq, NP]. Balanced split (partition_size = -S, S >= 2):
+    tmp_out [Hq, S + B, d], max_logits and exp_sums [Hq, S + B]."""
     dev = _dev(q, k_cache, v_cache, block_tables, context_lens, tmp_out, max_logits, exp_sums)
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    NP = num_partitions(MBS, bs, partition_size)
+    lead = (B, Hq) if partition_size > 0 else (Hq,)
     if tmp_out is None:
-        tmp_out = torch.empty((B, Hq, NP, d), dtype=torch.float32, device=dev)
-        max_logits = torch.empty((B, Hq, NP), dtype=torch.float32, device=dev)
-        exp_sums = torch.empty((B, Hq, NP), dtype=torch.float32, device=dev)
+        NP = num_partitions(MBS, bs, partition_size) if partition_size > 0 \
+            else -partition_size + B
+        tmp_out = torch.empty(lead + (NP, d), dtype=torch.float32, device=dev)
+        max_logits = torch.empty(lead + (NP,), dtype=torch.float32, device=dev)
+        exp_sums = torch.empty(lead + (NP,), dtype=torch.float32, device=dev)
     for t in (tmp_out, max_logits, exp_sums):
         if t.dtype != torch.float32:
             raise PaError("partials are float32")
-    if tmp_out.dim() != 4 or tmp_out.shape[:2] != (B, Hq) or tmp_out.shape[3] != d or \
-            max_logits.shape != tmp_out.shape[:3] or exp_sums.shape != tmp_out.shape[:3]:
+    n = len(lead)
+    if tmp_out.dim() != n + 2 or tuple(tmp_out.shape[:n]) != lead or tmp_out.shape[-1] != d or \
+            max_logits.shape != tmp_out.shape[:-1] or exp_sums.shape != tmp_out.shape[:-1]:
         raise PaError("partials have the wrong shape")
     _check(lib().pa_decode_partials(_ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
-                                    tmp_out.shape[2], _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    tmp_out.shape[n], _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs,
                                     NB, MBS, float(scale), dtype_code(q), dtype_code(k_cache),
                                     float(k_scale), float(v_scale), int(partition_size),
@@ -207,10 +227,15 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, partition_s
 def decode_reduce(tmp_out, max_logits, exp_sums, context_lens, partition_size: int,
                   out_dtype: torch.dtype = torch.bfloat16,
                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Merge split partials (C: pa_decode_reduce). Returns out [B, Hq, d]."""
+    """Merge split partials (C: pa_decode_reduce). Returns out [B, Hq, d]; the
+    partial layout follows partition_size as in decode_partials."""
     dev = _dev(tmp_out, max_logits, exp_sums, context_lens, out)
     _i32(context_lens, "context_lens")
-    B, Hq, NP, d = tmp_out.shape
+    B = context_lens.shape[0]
+    if partition_size > 0:
+        _, Hq, NP, d = tmp_out.shape
+    else:
+        Hq, NP, d = tmp_out.shape
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
     if out.dtype not in _TORCH_OF.values() or out.shape != (B, Hq, d):

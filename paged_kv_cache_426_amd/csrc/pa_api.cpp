@@ -35,14 +35,15 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
                        int kv_dtype, float k_scale, float v_scale, int partition_size) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL_POINTER;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0)
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
     return PA_ERR_BAD_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
   if (!known_dtype(q_dtype) || !known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
   if (!supported_head_dim(head_dim) || block_size != kSupportedBlockSize ||
       !supported_decode_pair(q_dtype, kv_dtype))
     return PA_ERR_UNSUPPORTED;
-  if (partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
+  if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
+  if (partition_size < 0 && num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return PA_ERR_BAD_SHAPE;
   if (kv_dtype == PA_FP8_E4M3FN && (!isfinite(k_scale) || !isfinite(v_scale)))
     return PA_ERR_BAD_SHAPE;
@@ -52,6 +53,7 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
   const int group = num_q_heads / num_kv_heads;
   const long long grid_y = (long long)num_kv_heads * (group / pa::heads_per_workgroup(group));
   if (grid_y > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (partition_size < -pa::kMaxAutoSplits) return PA_ERR_UNSUPPORTED;
   if ((long long)max_blocks_per_seq * block_size > INT_MAX) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
@@ -82,9 +84,29 @@ int pa_num_partitions(int max_blocks_per_seq, int block_size, int partition_size
 
 size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
                                 int max_blocks_per_seq, int block_size, int partition_size) {
-  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (partition_size == 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (partition_size < 0) {
+    // balanced split: per query head, one piece per (share, sequence) boundary
+    const size_t splits = partition_size == -1 ? (size_t)pa::kMaxAutoSplits
+                                               : (size_t)(-(long long)partition_size);
+    return (size_t)num_q_heads * (splits + (size_t)num_seqs) * ((size_t)head_dim + 2) *
+           sizeof(float);
+  }
   const size_t np = (size_t)pa_num_partitions(max_blocks_per_seq, block_size, partition_size);
   return (size_t)num_seqs * num_q_heads * np * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+int pa_decode_balanced_splits(int num_q_heads, int num_kv_heads, int head_dim, int q_dtype,
+                              int kv_dtype) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  if (!supported_head_dim(head_dim) || !supported_decode_pair(q_dtype, kv_dtype)) return 0;
+  pa::DecodeLaunch a{};
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  return pa::balanced_num_splits(a);
 }
 
 pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
@@ -100,8 +122,12 @@ pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
                               max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
                               partition_size);
   if (st != PA_OK) return st;
-  if (partition_size == 0) return PA_ERR_BAD_SHAPE;
-  if (max_partitions < pa_num_partitions(max_blocks_per_seq, block_size, partition_size))
+  // fixed partitions, or a balanced split with an explicit share count
+  if (partition_size == 0 || partition_size == -1) return PA_ERR_BAD_SHAPE;
+  if (partition_size > 0 &&
+      max_partitions < pa_num_partitions(max_blocks_per_seq, block_size, partition_size))
+    return PA_ERR_BAD_SHAPE;
+  if (partition_size < 0 && (long long)max_partitions < -(long long)partition_size + num_seqs)
     return PA_ERR_BAD_SHAPE;
   if (num_seqs == 0) return PA_OK;
   pa::DecodeLaunch a{};
@@ -126,6 +152,9 @@ pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
   a.partition_size = partition_size;
+  a.mode = partition_size > 0 ? pa::kSplitFixed : pa::kSplitBalanced;
+  a.num_splits = partition_size > 0 ? 0 : -partition_size;
+  a.direct = 0;
   return status_of(pa::launch_decode(a, stream));
 }
 
@@ -135,15 +164,36 @@ pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_log
                            int out_dtype, void *stream) {
   if (!out || !tmp_out || !max_logits || !exp_sums || !context_lens) return PA_ERR_NULL_POINTER;
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_partitions <= 0 ||
-      partition_size <= 0)
+      partition_size == 0 || partition_size == -1)
     return PA_ERR_BAD_SHAPE;
   if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
     return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535 || num_q_heads > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && partition_size % 16 != 0) return PA_ERR_BAD_SHAPE;
+  if (partition_size < 0) {
+    if (num_seqs > pa::kMaxBalancedSeqs || partition_size < -pa::kMaxAutoSplits)
+      return PA_ERR_UNSUPPORTED;
+    if ((long long)max_partitions < -(long long)partition_size + num_seqs) return PA_ERR_BAD_SHAPE;
+  }
   if (num_seqs == 0) return PA_OK;
-  return status_of(pa::launch_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs,
-                                     num_q_heads, head_dim, max_partitions, partition_size,
-                                     out_dtype, stream));
+  pa::ReduceLaunch r{};
+  r.out = out;
+  r.tmp_out = tmp_out;
+  r.max_logits = max_logits;
+  r.exp_sums = exp_sums;
+  r.context_lens = context_lens;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = head_dim;
+  r.block_size = 16;
+  r.max_partitions = max_partitions;
+  r.mode = partition_size > 0 ? pa::kSplitFixed : pa::kSplitBalanced;
+  r.partition_size = partition_size;
+  r.num_splits = partition_size > 0 ? 0 : -partition_size;
+  r.skip_single = 0;
+  r.out_dtype = out_dtype;
+  return status_of(pa::launch_reduce(r, stream));
 }
 
 pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -158,48 +208,77 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                               max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
                               partition_size);
   if (st != PA_OK) return st;
+  pa::DecodeLaunch a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  a.partition_size = partition_size;
+  a.direct = 1;
+  size_t need = 0;
+  size_t pieces = 0;  // partial-array entries per (sequence, head) or per head
   if (partition_size > 0) {
-    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim,
-                                                 max_blocks_per_seq, block_size, partition_size);
-    if (!workspace && need > 0) return PA_ERR_NULL_POINTER;
+    a.mode = pa::kSplitFixed;
+    a.max_partitions = pa_num_partitions(max_blocks_per_seq, block_size, partition_size);
+    pieces = (size_t)num_seqs * num_q_heads * a.max_partitions;
+    need = pieces * ((size_t)head_dim + 2) * sizeof(float);
+  } else if (partition_size < 0) {
+    a.mode = pa::kSplitBalanced;
+    // the workspace checks that need no device query come first
+    const size_t least = (size_t)num_q_heads * (1 + (size_t)num_seqs) * ((size_t)head_dim + 2) *
+                         sizeof(float);
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (workspace_bytes < least) return PA_ERR_WORKSPACE_TOO_SMALL;
+    a.num_splits = partition_size == -1 ? pa::balanced_num_splits(a) : -partition_size;
+    a.max_partitions = a.num_splits + num_seqs;
+    pieces = (size_t)num_q_heads * a.max_partitions;
+    need = pieces * ((size_t)head_dim + 2) * sizeof(float);
+  } else {
+    a.mode = pa::kSplitSingle;
+  }
+  if (need > 0) {
+    if (!workspace) return PA_ERR_NULL_POINTER;
     if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
   }
   if (num_seqs == 0) return PA_OK;
-  if (partition_size == 0) {
-    pa::DecodeLaunch a{};
-    a.out = out;
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.head_dim = head_dim;
-    a.block_size = block_size;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.scale = scale;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.q_dtype = q_dtype;
-    a.kv_dtype = kv_dtype;
-    a.partition_size = 0;
-    return status_of(pa::launch_decode(a, stream));
-  }
-  // split context: partials into the workspace, then the merge
-  const int np = pa_num_partitions(max_blocks_per_seq, block_size, partition_size);
-  const size_t nbh = (size_t)num_seqs * num_q_heads * np;
-  float *tmp_out = static_cast<float *>(workspace);
-  float *max_logits = tmp_out + nbh * head_dim;
-  float *exp_sums = max_logits + nbh;
-  st = pa_decode_partials(tmp_out, max_logits, exp_sums, np, q, k_cache, v_cache, block_tables,
-                          context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                          block_size, num_blocks, max_blocks_per_seq, scale, q_dtype, kv_dtype,
-                          k_scale, v_scale, partition_size, stream);
+  if (a.mode == pa::kSplitSingle) return status_of(pa::launch_decode(a, stream));
+  // split context: partials into the workspace (sequences held in one piece
+  // are written to `out` directly), then the merge
+  a.tmp_out = static_cast<float *>(workspace);
+  a.max_logits = a.tmp_out + pieces * head_dim;
+  a.exp_sums = a.max_logits + pieces;
+  st = status_of(pa::launch_decode(a, stream));
   if (st != PA_OK) return st;
-  return pa_decode_reduce(out, tmp_out, max_logits, exp_sums, context_lens, num_seqs,
-                          num_q_heads, head_dim, np, partition_size, q_dtype, stream);
+  pa::ReduceLaunch r{};
+  r.out = out;
+  r.tmp_out = a.tmp_out;
+  r.max_logits = a.max_logits;
+  r.exp_sums = a.exp_sums;
+  r.context_lens = context_lens;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = head_dim;
+  r.block_size = block_size;
+  r.max_partitions = a.max_partitions;
+  r.mode = a.mode;
+  r.partition_size = partition_size;
+  r.num_splits = a.num_splits;
+  r.skip_single = 1;
+  r.out_dtype = q_dtype;
+  return status_of(pa::launch_reduce(r, stream));
 }
 
 pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache, void *v_cache,

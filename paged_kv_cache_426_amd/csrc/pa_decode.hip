@@ -7,41 +7,48 @@
 // deep dive" §2.1; "vLLM inference principles", block-table figure), and
 // query head h reads KV head h / group ("KV-Cache evolution" §3A, GQA).
 //
-// Work decomposition. One workgroup (4 waves) serves one (sequence, KV head,
-// run of GH query heads of that KV head's group, token range). The token
-// range is the whole context (single pass) or one partition of P tokens
-// (split context, followed by reduce_kernel). Because the GH query heads of a
-// group share one KV head, each K/V byte of the range is read from HBM once
-// and used GH times; the GH query rows live in registers of every lane.
+// Work decomposition. A workgroup (4 waves) serves one KV head and a run of
+// GH of its query heads, over a range of that KV head's cache blocks: a whole
+// sequence (single pass), one fixed-size partition of a sequence (split
+// context), or an equal share of all blocks of all sequences taken end to end
+// (balanced split: every workgroup reads the same number of blocks, so the
+// grid finishes in one round whatever the length mix). Each K/V byte of the
+// range is read from HBM once and used for all GH heads.
 //
-// The range is walked in chunks; each wave owns `bpw` whole blocks of a chunk.
-// Lanes are laid out so that one 16-byte load per lane covers `tpi` token
-// rows: lane = r * lpt + c reads bytes [16c, 16c+16) of token row r, so each
-// row is read by lpt adjacent lanes in one coalesced access. Per chunk:
-//   A. every wave issues all its K and V loads (gathered through the block
-//      table, the physical id being a wave-uniform scalar load), then forms
-//      the partial dot products of its K rows with the GH query rows and sums
-//      them across the lpt lanes of a row with DPP (no LDS); logits (log2
-//      domain) go to LDS;
-//   B. one wave per head turns the chunk's logits into exp2(s - m_new) in
-//      place, with the running max m and sum l kept in LDS (online softmax
-//      across chunks, rescale factor alpha = exp2(m_old - m_new));
-//   C. every wave rescales its fp32 accumulators by alpha and adds p * V for
-//      its rows.
-// At the end the accumulators are summed across rows (shuffles) and waves
-// (LDS) and either normalised into `out` or written as split partials.
+// Inside a range, the waves take units of NBI blocks round-robin and run
+// independently, each with its own online softmax; the next unit's K/V are
+// loaded into registers while the current one is computed. Per unit:
+//   * logits: one 16x16 MFMA tile per block, rows = query heads (row m holds
+//     head m % GH), columns = the block's 16 tokens, reduced over head_dim in
+//     D/32 steps (16-bit types; fp8 K is first widened exactly to the query's
+//     type) or D/4 steps (fp32). Lane l loads token l%16's row elements
+//     [D/4 * (l/16), +D/4) -- 64 contiguous bytes for bf16 d=128 -- and the
+//     query fragment of each lane covers the same elements, so the product is
+//     the full dot product whatever the MFMA's internal k order;
+//   * online softmax: block max over the 16 token lanes with DPP, running max
+//     m and per-lane partial sums l, rescale alpha = exp2(m_old - m_new);
+//   * P.V on the vector ALU: lane (r, c) of a V load holds 8 elements
+//     [8c, 8c+8) of token row r; the probabilities reach that layout through
+//     a small per-wave LDS buffer; fp32 accumulators acc[head][8].
+// At the end of a range the waves' (m, l, acc) are merged in LDS, in fixed
+// wave order, and written as the output or as one split partial.
 //
 // Masking: tokens at or beyond the range end get a logit of -inf (a select,
 // never a product, so stale or NaN cache contents cannot leak in), and their
 // V words are zeroed before use. Block-table entries past the range end are
-// never read; loads of such blocks are redirected to the range's first block.
+// never read; loads for such blocks are redirected to the range's first block.
 //
-// The arithmetic order depends only on logical token positions, never on
-// physical block ids: results are bitwise invariant under any relabelling of
-// physical blocks and identical for aliased and private copies of a block.
+// The arithmetic order depends only on logical token positions (and, in the
+// balanced split, on the context lengths), never on physical block ids:
+// results are bitwise invariant under any relabelling of physical blocks and
+// identical for aliased and private copies of a block.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -49,11 +56,17 @@
 namespace pa {
 namespace {
 
-constexpr int kBlockSize = 16;
-constexpr int kWaves = 4;
+constexpr int kBs = 16;  // tokens per cache block
+constexpr int kStages = 2;  // register stages of the load pipeline
+constexpr int kWaves = 2;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct DecodeParams {
   void *out;
@@ -65,28 +78,177 @@ struct DecodeParams {
   const uint8_t *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
+  int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int max_blocks_per_seq;
-  int max_partitions;
-  int partition_size;  // 0: whole context
-  int group;           // query heads per KV head
-  float scale_log2;    // scale * k_scale * log2(e)
+  int mode;              // kSplitSingle / kSplitFixed / kSplitBalanced
+  int partition_blocks;  // fixed / single: blocks per partition
+  int max_partitions;    // stride of the partial arrays (see DecodeLaunch)
+  int num_splits;        // balanced: number of shares S
+  int direct;            // a range that is a whole sequence writes `out` directly
+  int group;             // query heads per KV head
+  float scale_log2;      // scale * k_scale * log2(e)
   float v_scale;
 };
 
-// Lane geometry for a cache element type and head size.
-template <int KT, int D>
+// ---------------------------------------------------------------------------
+// per-type geometry
+// ---------------------------------------------------------------------------
+
+template <int QT, int KT, int D>
 struct Geo {
-  static constexpr int kb = ElemBytes<KT>::value;
-  static constexpr int epl = 16 / kb;                    // cache elements per 16-byte load
-  static constexpr int lpt = D / epl;                    // lanes per token row
-  static constexpr int tpi = kWave / lpt;                // token rows per wave load
-  static constexpr int nlb = kBlockSize / tpi;           // loads per lane per block
-  static constexpr int bpw = nlb >= 8 ? 1 : 8 / nlb;     // blocks per wave per chunk
-  static constexpr int chunk = kWaves * bpw * kBlockSize;
-  static_assert(lpt >= 1 && lpt <= kWave && tpi <= kBlockSize, "unsupported geometry");
+  static constexpr int kb = ElemBytes<KT>::value;   // cache element bytes
+  static constexpr int row = D * kb;                // bytes of one head's row
+  // K in the MFMA operand layout: lane l holds token l%16; its piece i is
+  // row bytes k_byte(i, l/16) = [64 i + 16 jq, +16)
+  static constexpr int k_lane_bytes = D / 4 * kb;
+  static constexpr int nkl = k_lane_bytes / 16;     // 16-byte K pieces per lane per block
+  static __device__ __forceinline__ uint32_t k_byte(int i, int jq) { return 64 * i + 16 * jq; }
+  // first element of MFMA step s for lane group jq (8 consecutive elements,
+  // or one for fp32)
+  static __device__ __forceinline__ int q_elem(int s, int jq) {
+    if constexpr (QT == PA_F32) return 16 * (s / 4) + 4 * jq + s % 4;
+    else if constexpr (kb == 1) return 64 * (s / 2) + 16 * jq + 8 * (s % 2);
+    else return 32 * s + 8 * jq;
+  }
+  static constexpr int ksteps = (QT == PA_F32) ? D / 4 : D / 32;  // MFMAs per block
+  // V, accumulate layout: lane (r, c) holds elements [8c, 8c+8) of row r
+  static constexpr int v_piece = 8 * kb;            // bytes per lane per V load
+  static constexpr int lpt = D / 8;                 // lanes per token row
+  static constexpr int rv = kWave / lpt;            // token rows per V load
+  static constexpr int nvl = kBs / rv;              // V loads per lane per block
+  // K global loads are row-contiguous like V (16 bytes per lane, lanes of a
+  // quad on adjacent bytes, so each quad is one cache access): lane (rk, ck)
+  // of load i reads bytes [16 ck, +16) of row i * rvk + rk. The tile then
+  // goes through LDS, rows padded by 16 bytes (the 16 rows of a transposed
+  // read land in distinct banks), into the MFMA operand layout.
+  static constexpr int lpk = row / 16;              // lanes per row of a K load
+  static constexpr int rvk = kWave / lpk;           // rows per K load
+  static constexpr int krs = row + 16;              // LDS row stride of the K tile
+  static_assert(nkl >= 1 && nvl >= 1 && rvk * nkl == kBs, "unsupported geometry");
 };
+
+template <int QT> struct QOpT { using type = u32x4; };  // 8 x 16-bit
+template <> struct QOpT<PA_F32> { using type = float; };
+
+// One V load: 8 cache elements.
+template <int KT> struct VPiece { uint32_t w[2 * ElemBytes<KT>::value]; };
+
+// Buffer resources: the hardware range check of a raw buffer load returns
+// zeros without touching memory for bytes at or beyond num_records, which
+// turns the loads of units past a range's end into no-ops while keeping every
+// load instruction unconditional (one resource per block and cache).
+constexpr int kRsrcFlags = 0x00020000;  // gfx9 word 3: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
+                                           kRsrcFlags);
+}
+
+// K and V are streamed once: loads carry the non-temporal hint (aux bit 1,
+// "nt" on gfx950), which measurably raises the sustained read rate.
+constexpr int kLoadAux = 2;
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux);
+}
+
+template <int KT>
+__device__ __forceinline__ void buf_load_v(VPiece<KT> &pc, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (ElemBytes<KT>::value == 4) {
+    const u32x4 a = buf_load16(r, off);
+    const u32x4 b = buf_load16(r, off + 16);
+    pc.w[0] = a.x; pc.w[1] = a.y; pc.w[2] = a.z; pc.w[3] = a.w;
+    pc.w[4] = b.x; pc.w[5] = b.y; pc.w[6] = b.z; pc.w[7] = b.w;
+  } else if constexpr (ElemBytes<KT>::value == 2) {
+    const u32x4 a = buf_load16(r, off);
+    pc.w[0] = a.x; pc.w[1] = a.y; pc.w[2] = a.z; pc.w[3] = a.w;
+  } else {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadAux);
+    pc.w[0] = a.x; pc.w[1] = a.y;
+  }
+}
+
+// 8 V elements -> fp32; all zero when the token is masked.
+template <int KT>
+__device__ __forceinline__ void widen_v(const VPiece<KT> &pc, bool ok, float (&x)[8]) {
+  constexpr int NW = 2 * ElemBytes<KT>::value;
+  uint32_t w[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w[i] = ok ? pc.w[i] : 0u;
+  if constexpr (KT == PA_F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = u2f(w[i]);
+  } else if constexpr (KT == PA_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else if constexpr (KT == PA_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = f16_lo(w[i]);
+      x[2 * i + 1] = f16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+      x[4 * i] = lo.x;
+      x[4 * i + 1] = lo.y;
+      x[4 * i + 2] = hi.x;
+      x[4 * i + 3] = hi.y;
+    }
+  }
+}
+
+// fp8 pair (bytes 0,1 or 2,3 of a word) widened exactly to the query's 16-bit type
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t fp8_pair_to_16(uint32_t w) {
+  if constexpr (QT == PA_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+}
+
+// B operand of MFMA step s from the lane's K loads of one block.
+template <int QT, int KT, int D>
+__device__ __forceinline__ typename QOpT<QT>::type k_operand(const u32x4 *k, int s) {
+  if constexpr (QT == PA_F32) {
+    const u32x4 w = k[s / 4];
+    const int t = s % 4;
+    return u2f(t == 0 ? w.x : t == 1 ? w.y : t == 2 ? w.z : w.w);
+  } else if constexpr (KT == PA_FP8_E4M3FN) {
+    const u32x4 w = k[s / 2];
+    const uint32_t a = (s % 2) ? w.z : w.x;
+    const uint32_t b = (s % 2) ? w.w : w.y;
+    u32x4 r;
+    r.x = fp8_pair_to_16<QT, false>(a);
+    r.y = fp8_pair_to_16<QT, true>(a);
+    r.z = fp8_pair_to_16<QT, false>(b);
+    r.w = fp8_pair_to_16<QT, true>(b);
+    return r;
+  } else {
+    return k[s];
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ f32x4 mfma(typename QOpT<QT>::type a, typename QOpT<QT>::type b,
+                                      f32x4 c) {
+  if constexpr (QT == PA_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else if constexpr (QT == PA_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+}
 
 template <int QT>
 __device__ __forceinline__ void store_elem(void *out, size_t idx, float v) {
@@ -99,380 +261,564 @@ __device__ __forceinline__ void store_elem(void *out, size_t idx, float v) {
   }
 }
 
-// 16 cache bytes -> fp32 elements.
-template <int KT>
-__device__ __forceinline__ void widen(const u32x4 w, float *v) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (KT == PA_F32) {
-      v[i] = u2f(ws[i]);
-    } else if constexpr (KT == PA_BF16) {
-      v[2 * i] = bf16_lo(ws[i]);
-      v[2 * i + 1] = bf16_hi(ws[i]);
-    } else if constexpr (KT == PA_F16) {
-      v[2 * i] = f16_lo(ws[i]);
-      v[2 * i + 1] = f16_hi(ws[i]);
-    } else {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], true);
-      v[4 * i] = lo.x;
-      v[4 * i + 1] = lo.y;
-      v[4 * i + 2] = hi.x;
-      v[4 * i + 3] = hi.y;
-    }
-  }
+// Orders a wave's LDS accesses (one wave writes and reads its own region;
+// LDS instructions of a wave execute in order, so a compiler fence suffices).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-// The query fragment of one lane for one head, in the form the dot product
-// consumes: packed 16-bit pairs for 16-bit and fp8 caches (fp8 K is widened
-// exactly to the query's 16-bit type), fp32 for fp32 caches.
-template <int QT, int KT>
-struct QFrag {
-  static constexpr int words = (KT == PA_FP8_E4M3FN) ? 8 : 4;
-  uint32_t w[words];
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+
+template <int QT, int KT, int D, int GH, int NBI>
+struct Shared {
+  float p[kWaves][NBI * kBs][GH];   // probabilities of the current unit
+  float alpha[kWaves][GH];          // rescale factor of the current unit
+  float m[kWaves][GH];              // per-wave softmax state at the end of a range
+  float l[kWaves][GH];
+  float acc[kWaves][GH][D];
+  // K tiles of the current unit, one per wave and block
+  uint8_t kt[kWaves][NBI][kBs * (D * ElemBytes<KT>::value + 16)] __attribute__((aligned(16)));
+  int start[kMaxBalancedSeqs + 1];  // balanced split: first block of each sequence
+  int wave_sum[kWaves];
 };
 
-template <int QT, int KT, int D>
-__device__ __forceinline__ void load_q(QFrag<QT, KT> &f, const uint8_t *qrow, int c) {
-  // qrow points at element 0 of one query head
-  if constexpr (KT == PA_FP8_E4M3FN) {
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(qrow + c * 32);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(qrow + c * 32 + 16);
-    f.w[0] = a.x; f.w[1] = a.y; f.w[2] = a.z; f.w[3] = a.w;
-    f.w[4] = b.x; f.w[5] = b.y; f.w[6] = b.z; f.w[7] = b.w;
-  } else {
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(qrow + c * 16);
-    f.w[0] = a.x; f.w[1] = a.y; f.w[2] = a.z; f.w[3] = a.w;
-  }
-}
+template <int QT, int KT, int D, int GH, int NBI>
+struct Stage {
+  using G = Geo<QT, KT, D>;
+  u32x4 k[NBI][G::nkl];
+  VPiece<KT> v[NBI][G::nvl];
+};
 
-// fp8 pair (byte half `hi` of a word) widened exactly to a 16-bit pair
-template <int QT, bool HI>
-__device__ __forceinline__ uint32_t fp8_pair_to_16(uint32_t w) {
-  if constexpr (QT == PA_BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-  }
-}
-
-template <int QT>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
-  if constexpr (QT == PA_BF16) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), acc, false);
-  } else {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
-                                  acc, false);
-  }
-}
-
-// Partial dot products of one 16-byte K piece with the GH query fragments.
-template <int QT, int KT, int GH>
-__device__ __forceinline__ void partial_dots(const u32x4 k, const QFrag<QT, KT> (&qf)[GH],
-                                             float (&out)[GH]) {
-  const uint32_t ks[4] = {k.x, k.y, k.z, k.w};
-  if constexpr (KT == PA_F32) {
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float s = u2f(qf[h].w[0]) * u2f(ks[0]);
-      s = fmaf(u2f(qf[h].w[1]), u2f(ks[1]), s);
-      s = fmaf(u2f(qf[h].w[2]), u2f(ks[2]), s);
-      s = fmaf(u2f(qf[h].w[3]), u2f(ks[3]), s);
-      out[h] = s;
-    }
-  } else if constexpr (KT == PA_FP8_E4M3FN) {
-    uint32_t k16[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      k16[2 * i] = fp8_pair_to_16<QT, false>(ks[i]);
-      k16[2 * i + 1] = fp8_pair_to_16<QT, true>(ks[i]);
-    }
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s = dot2<QT>(k16[i], qf[h].w[i], s);
-      out[h] = s;
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s = dot2<QT>(ks[i], qf[h].w[i], s);
-      out[h] = s;
-    }
-  }
-}
-
-template <int QT, int KT, int D, int GH>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
-  using G = Geo<KT, D>;
-  constexpr int EPL = G::epl, LPT = G::lpt, TPI = G::tpi, NLB = G::nlb, BPW = G::bpw;
-  constexpr int CH = G::chunk;
+// One range [blo, bhi) of the blocks of sequence b, all waves.
+template <int QT, int KT, int D, int GH, int NBI, int NS>
+__device__ __forceinline__ void run_range(const DecodeParams &p,
+                                          Shared<QT, KT, D, GH, NBI> &sh, int b, int blo,
+                                          int bhi, int piece, bool whole, int h0, int g) {
+  using G = Geo<QT, KT, D>;
+  using QOp = typename QOpT<QT>::type;
+  using St = Stage<QT, KT, D, GH, NBI>;
   constexpr int QB = ElemBytes<QT>::value;
-
-  __shared__ float s_p[2][CH * GH];  // logits, then probabilities; double-buffered per chunk
-  __shared__ float s_m[GH], s_l[GH], s_alpha[GH];
-  __shared__ float s_o[kWaves][GH][D];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane / LPT;
-  const int c = lane % LPT;
-
-  const int b = blockIdx.z;
-  const int hg = blockIdx.y;
-  const int part = blockIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int jq = lane >> 4;  // MFMA lane group
+  const int tl = lane & 15;  // MFMA column: token within a block
+  const int r = lane / G::lpt;  // V layout: token row within a load
+  const int c = lane % G::lpt;  // V layout: 8-element column group
+  b = uniform(b);
+  blo = uniform(blo);
+  bhi = uniform(bhi);
+  const int n = uniform(p.context_lens[b]);
+  const int tok_lim = min(bhi * kBs, n);
+  const int nunits = (bhi - blo + NBI - 1) / NBI;
   const int Hq = p.num_q_heads;
-  const int g = hg / (p.group / GH);
-  const int h0 = hg * GH;
-  const int n = p.context_lens[b];
 
-  int start = 0, end = n;
-  if (p.partition_size > 0) {
-    start = part * p.partition_size;
-    if (start >= n) return;
-    end = min(n, start + p.partition_size);
-  } else if (n <= 0) {
-    for (int i = tid; i < GH * D; i += kThreads)
-      store_elem<QT>(p.out, ((size_t)b * Hq + h0) * D + i, 0.0f);
-    return;
-  }
-
-  if (tid < GH) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.0f;
-  }
-
-  QFrag<QT, KT> qf[GH];
+  // query fragments (A operand): row tl holds head h0 + tl % GH
+  QOp qa[G::ksteps];
   {
-    const uint8_t *qb = p.q + ((size_t)b * Hq + h0) * D * QB;
+    const uint8_t *qrow = p.q + ((size_t)b * Hq + h0 + tl % GH) * D * QB;
+    if constexpr (QT == PA_F32) {
+      const float *qf = reinterpret_cast<const float *>(qrow);
 #pragma unroll
-    for (int h = 0; h < GH; ++h) load_q<QT, KT, D>(qf[h], qb + (size_t)h * D * QB, c);
+      for (int s = 0; s < G::ksteps; s += 4) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(qf + G::q_elem(s, jq));
+        qa[s] = u2f(w.x);
+        qa[s + 1] = u2f(w.y);
+        qa[s + 2] = u2f(w.z);
+        qa[s + 3] = u2f(w.w);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < G::ksteps; ++s)
+        qa[s] = *reinterpret_cast<const u32x4 *>(qrow + G::q_elem(s, jq) * QB);
+    }
   }
 
-  float acc[GH][EPL];
+  float m[4], l[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.0f;
+  }
+  float acc[GH][8];
 #pragma unroll
   for (int h = 0; h < GH; ++h)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
 
-  const uint32_t row_bytes = (uint32_t)p.num_kv_heads * D * G::kb;
-  const size_t blk_bytes = (size_t)row_bytes * kBlockSize;
-  const uint32_t lane_off = r * row_bytes + c * 16;
-  const uint8_t *kg = p.k_cache + (size_t)g * D * G::kb;
-  const uint8_t *vg = p.v_cache + (size_t)g * D * G::kb;
-  const int32_t *bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
-  const int first_blk = start / kBlockSize;
+  const uint32_t rowstride = (uint32_t)p.num_kv_heads * G::row;
+  const uint32_t blk_bytes = rowstride * kBs;          // < 2^31, checked on the host
+  const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;  // head g's row 0 to block end
+  const uint32_t k_off = (lane / G::lpk) * rowstride + (lane % G::lpk) * 16;
+  uint32_t v_off[G::nvl];
+#pragma unroll
+  for (int i = 0; i < G::nvl; ++i) v_off[i] = (i * G::rv + r) * rowstride + c * G::v_piece;
+  const uint8_t *kbase = p.k_cache + (size_t)g * G::row;
+  const uint8_t *vbase = p.v_cache + (size_t)g * G::row;
+  const int32_t *btg = p.block_tables + (size_t)b * p.max_blocks_per_seq;
   const float sl2 = p.scale_log2;
 
-  __syncthreads();
-
-  int buf = 0;
-  for (int cs = start; cs < end; cs += CH, buf ^= 1) {
-    const int wb0 = cs / kBlockSize + wave * BPW;
-    float *sp = s_p[buf];
-
-    u32x4 kr[BPW][NLB], vr[BPW][NLB];
+  // Block ids of the wave's units, one chunk of kIdsUnits units at a time:
+  // lane i of `ids` holds the id of block i % NBI of unit k0 + i / NBI, read
+  // with readlane (no memory wait) when that unit's loads are issued.
+  constexpr int kIdsUnits = kWave / NBI;
+  int ids = 0;
+  // Loads of the wave's unit k (chunk starting at k0) into a register stage;
+  // a unit past the end (valid false) loads nothing.
+  auto issue = [&](int k, int k0, bool valid, St &st) {
 #pragma unroll
-    for (int bi = 0; bi < BPW; ++bi) {
-      const int j = wb0 + bi;
-      const int phys = bt[(j * kBlockSize < end) ? j : first_blk];
-      const uint8_t *kb = kg + (size_t)phys * blk_bytes;
-      const uint8_t *vb = vg + (size_t)phys * blk_bytes;
+    for (int bi = 0; bi < NBI; ++bi) {
+      const int lidx = min((k - k0) * NBI + bi, kWave - 1);
+      const int id = __builtin_amdgcn_readlane(ids, lidx);
+      const size_t off = (size_t)id * blk_bytes;
+      const uint32_t n = valid ? blk_span : 0u;
+      const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase + off, n);
+      const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase + off, n);
 #pragma unroll
-      for (int i = 0; i < NLB; ++i)
-        kr[bi][i] = *reinterpret_cast<const u32x4 *>(kb + (size_t)i * TPI * row_bytes + lane_off);
+      for (int i = 0; i < G::nkl; ++i) st.k[bi][i] = buf_load16(rk, k_off + i * G::rvk * rowstride);
 #pragma unroll
-      for (int i = 0; i < NLB; ++i)
-        vr[bi][i] = *reinterpret_cast<const u32x4 *>(vb + (size_t)i * TPI * row_bytes + lane_off);
+      for (int i = 0; i < G::nvl; ++i) buf_load_v<KT>(st.v[bi][i], rv, v_off[i]);
     }
+  };
 
-    // A: logits of this wave's rows
+  auto compute_unit = [&](int k, const St &st) {
+    const int jb = blo + (wave + k * kWaves) * NBI;
+    // logits, log2 domain; masked tokens -inf
+    float sv[NBI][4];
+    // K tile: registers (row-contiguous) -> LDS -> MFMA operand layout, in
+    // which lane (tl, jq) holds bytes k_byte(i, jq) of token row tl
 #pragma unroll
-    for (int bi = 0; bi < BPW; ++bi) {
-      const int j = wb0 + bi;
+    for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
-      for (int i = 0; i < NLB; ++i) {
-        const int tl = (wave * BPW + bi) * kBlockSize + i * TPI + r;
-        const bool valid = j * kBlockSize + i * TPI + r < end;
-        float d[GH];
-        partial_dots<QT, KT, GH>(kr[bi][i], qf, d);
+      for (int i = 0; i < G::nkl; ++i)
+        *reinterpret_cast<u32x4 *>(&sh.kt[wave][bi][(i * G::rvk + lane / G::lpk) * G::krs +
+                                                    (lane % G::lpk) * 16]) = st.k[bi][i];
+    wave_lds_fence();
 #pragma unroll
-        for (int h = 0; h < GH; ++h) d[h] = group_sum<LPT>(d[h]);
+    for (int bi = 0; bi < NBI; ++bi) {
+      u32x4 kop[G::nkl];
 #pragma unroll
-        for (int hh = 0; hh < GH; hh += LPT) {
-          float v = d[hh];
+      for (int i = 0; i < G::nkl; ++i)
+        kop[i] = *reinterpret_cast<const u32x4 *>(&sh.kt[wave][bi][tl * G::krs + G::k_byte(i, jq)]);
+      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int x = 1; x < LPT && hh + x < GH; ++x) v = (c == x) ? d[hh + x] : v;
-          if (hh + c < GH) sp[tl * GH + hh + c] = valid ? v * sl2 : -INFINITY;
-        }
-      }
+      for (int s = 0; s < G::ksteps; ++s) d = mfma<QT>(qa[s], k_operand<QT, KT, D>(kop, s), d);
+      const bool ok = (jb + bi) * kBs + tl < tok_lim;
+      sv[bi][0] = ok ? d.x * sl2 : -INFINITY;
+      sv[bi][1] = ok ? d.y * sl2 : -INFINITY;
+      sv[bi][2] = ok ? d.z * sl2 : -INFINITY;
+      sv[bi][3] = ok ? d.w * sl2 : -INFINITY;
     }
-    __syncthreads();
-
-    // B: chunk softmax statistics, one wave per head
-    for (int h = wave; h < GH; h += kWaves) {
-      constexpr int PER = CH / kWave;
-      float s[PER];
-      float mx = -INFINITY;
+    // online softmax per MFMA row v (head (4*jq + v) % GH)
+    float al[4];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        s[k] = sp[(lane + k * kWave) * GH + h];
-        mx = fmaxf(mx, s[k]);
-      }
-      mx = group_max<kWave>(mx);
-      const float m_old = s_m[h];
-      const float m_new = fmaxf(m_old, mx);
+    for (int v = 0; v < 4; ++v) {
+      float mx = sv[0][v];
+#pragma unroll
+      for (int bi = 1; bi < NBI; ++bi) mx = fmaxf(mx, sv[bi][v]);
+      mx = group_max<16>(mx);
+      const float mn = fmaxf(m[v], mx);
+      al[v] = __builtin_amdgcn_exp2f(m[v] - mn);
+      m[v] = mn;
       float sum = 0.0f;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const float e = __builtin_amdgcn_exp2f(s[k] - m_new);
-        sp[(lane + k * kWave) * GH + h] = e;
+      for (int bi = 0; bi < NBI; ++bi) {
+        const float e = __builtin_amdgcn_exp2f(sv[bi][v] - mn);
+        sv[bi][v] = e;
         sum += e;
       }
-      sum = group_sum<kWave>(sum);
-      if (lane == 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
-        s_alpha[h] = alpha;
-        s_l[h] = s_l[h] * alpha + sum;
-        s_m[h] = m_new;
+      l[v] = l[v] * al[v] + sum;
+    }
+    // hand the probabilities and alpha to the V layout
+    if (4 * jq < GH) {
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (v < GH) sh.p[wave][bi * kBs + tl][4 * jq + v] = sv[bi][v];
+      if (tl == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (v < GH) sh.alpha[wave][4 * jq + v] = al[v];
       }
     }
-    __syncthreads();
-
-    // C: rescale and accumulate p * V
+    wave_lds_fence();
     {
-      float al[GH];
+      float a[GH];
 #pragma unroll
-      for (int h = 0; h < GH; ++h) al[h] = s_alpha[h];
+      for (int h = 0; h < GH; ++h) a[h] = sh.alpha[wave][h];
 #pragma unroll
       for (int h = 0; h < GH; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+        for (int e = 0; e < 8; ++e) acc[h][e] *= a[h];
     }
 #pragma unroll
-    for (int bi = 0; bi < BPW; ++bi) {
-      const int j = wb0 + bi;
-      const bool full = (j + 1) * kBlockSize <= end;
+    for (int bi = 0; bi < NBI; ++bi) {
 #pragma unroll
-      for (int i = 0; i < NLB; ++i) {
-        const int tl = (wave * BPW + bi) * kBlockSize + i * TPI + r;
-        u32x4 w = vr[bi][i];
-        if (!full) {
-          const bool valid = j * kBlockSize + i * TPI + r < end;
-          w.x = valid ? w.x : 0u;
-          w.y = valid ? w.y : 0u;
-          w.z = valid ? w.z : 0u;
-          w.w = valid ? w.w : 0u;
-        }
-        float v[EPL];
-        widen<KT>(w, v);
+      for (int i = 0; i < G::nvl; ++i) {
+        const int t = i * G::rv + r;
+        const bool ok = (jb + bi) * kBs + t < tok_lim;
+        float x[8];
+        widen_v<KT>(st.v[bi][i], ok, x);
         float pw[GH];
 #pragma unroll
-        for (int h = 0; h < GH; ++h) pw[h] = sp[tl * GH + h];
+        for (int h = 0; h < GH; ++h) pw[h] = sh.p[wave][bi * kBs + t][h];
 #pragma unroll
         for (int h = 0; h < GH; ++h)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw[h], v[e], acc[h][e]);
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], x[e], acc[h][e]);
+      }
+    }
+    wave_lds_fence();
+  };
+
+  // The wave's units k = 0 .. nk-1 (unit wave + k * kWaves of the range)
+  // through NS register stages in turn: while unit k is computed, the loads
+  // of units k+1 .. k+NS-1 are in flight. Every load instruction is issued
+  // unconditionally (past the end they read nothing), so the compiler's
+  // memory-counter waits stay exact: computing unit k waits only for unit k.
+  const int nk = wave < nunits ? (nunits - wave + kWaves - 1) / kWaves : 0;
+  for (int k0 = 0; k0 < nk; k0 += kIdsUnits) {
+    const int kn = min(nk - k0, kIdsUnits);
+    {
+      const int kk = k0 + lane / NBI;
+      const int j = blo + (wave + kk * kWaves) * NBI + lane % NBI;
+      ids = btg[(kk < nk && j < bhi) ? j : blo];
+    }
+    St st[NS];
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(k0 + s, k0, s < kn, st[s]);
+    for (int k = 0; k < kn; k += NS) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        issue(k0 + k + s + NS - 1, k0, k + s + NS - 1 < kn, st[(s + NS - 1) % NS]);
+        if (k + s < kn) compute_unit(k0 + k + s, st[s]);
       }
     }
   }
 
-  // sum the accumulators over the rows of a wave, then over the waves
+  // merge the waves: sums over the token lanes / rows, then across waves
+#pragma unroll
+  for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
+  if (4 * jq < GH && tl == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (v < GH) {
+        sh.m[wave][4 * jq + v] = m[v];
+        sh.l[wave][4 * jq + v] = l[v];
+      }
+  }
 #pragma unroll
   for (int h = 0; h < GH; ++h)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e)
+    for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int off = LPT; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
+      for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < GH; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[wave][h][c * EPL + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) sh.acc[wave][h][c * 8 + e] = acc[h][e];
   }
   __syncthreads();
 
+  const bool to_out = whole && p.direct;
   for (int i = tid; i < GH * D; i += kThreads) {
     const int h = i / D, d = i % D;
-    float o = 0.0f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += s_o[w][h][d];
-    const float l = s_l[h];
-    const float res = o * p.v_scale / l;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.m[w][h]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = __builtin_amdgcn_exp2f(sh.m[w][h] - M);
+      L += sh.l[w][h] * sc;
+      O += sh.acc[w][h][d] * sc;
+    }
+    const float res = O * p.v_scale / L;
     const size_t bh = (size_t)b * Hq + h0 + h;
-    if (p.partition_size > 0) {
-      const size_t pi = bh * p.max_partitions + part;
+    if (to_out) {
+      store_elem<QT>(p.out, bh * D + d, res);
+    } else {
+      const size_t pi = (p.mode == kSplitBalanced)
+                            ? (size_t)(h0 + h) * p.max_partitions + piece
+                            : bh * p.max_partitions + piece;
       p.tmp_out[pi * D + d] = res;
       if (d == 0) {
-        p.max_logits[pi] = s_m[h] * kLn2;
-        p.exp_sums[pi] = l;
+        p.max_logits[pi] = M * kLn2;
+        p.exp_sums[pi] = L;
       }
-    } else {
-      store_elem<QT>(p.out, bh * D + d, res);
     }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int num_blocks_of(int n) { return n > 0 ? (n + kBs - 1) / kBs : 0; }
+
+template <int QT, int KT, int D, int GH, int NBI, int NS>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
+  __shared__ Shared<QT, KT, D, GH, NBI> sh;
+  const int tid = threadIdx.x;
+  const int h0 = blockIdx.y * GH;  // first query head of this workgroup
+  const int g = h0 / p.group;      // its KV head
+
+  if (p.mode != kSplitBalanced) {
+    const int b = blockIdx.z;
+    const int part = blockIdx.x;
+    const int n = p.context_lens[b];
+    if (n <= 0) {
+      if (p.mode == kSplitSingle)
+        for (int i = tid; i < GH * D; i += kThreads)
+          store_elem<QT>(p.out, ((size_t)b * p.num_q_heads + h0) * D + i, 0.0f);
+      return;
+    }
+    const int nblk = num_blocks_of(n);
+    const int blo = part * p.partition_blocks;
+    if (blo >= nblk) return;
+    const int bhi = min(nblk, blo + p.partition_blocks);
+    run_range<QT, KT, D, GH, NBI, NS>(p, sh, b, blo, bhi, part, nblk <= p.partition_blocks, h0, g);
+    return;
+  }
+
+  // Balanced split: the blocks of all sequences, end to end, cut into
+  // num_splits equal shares; share s = blockIdx.x. First the start block of
+  // every sequence (exclusive prefix sum of ceil(n / 16)).
+  const int B = p.num_seqs;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  {
+    constexpr int PER = kMaxBalancedSeqs / kThreads;
+    int cnt[PER];
+    int tot = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int bb = PER * tid + k;
+      cnt[k] = bb < B ? num_blocks_of(p.context_lens[bb]) : 0;
+      tot += cnt[k];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) sh.wave_sum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += sh.wave_sum[w];
+    int ex = base + incl - tot;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int bb = PER * tid + k;
+      if (bb < B) sh.start[bb] = ex;
+      ex += cnt[k];
+    }
+    if (tid == kThreads - 1) sh.start[B] = base + incl;
+    __syncthreads();
+  }
+  const int total = sh.start[B];
+  // at most one share per block, so that no share is empty
+  const int S = min(p.num_splits, total);
+  const int s = blockIdx.x;
+  if (s >= S) return;
+  const int lo = (int)((long long)s * total / S);
+  const int hi = (int)((long long)(s + 1) * total / S);
+  if (lo >= hi) return;
+  // the sequence holding block lo: the largest b with start[b] <= lo
+  int bl = 0, bh = B - 1;
+  while (bl < bh) {
+    const int mid = (bl + bh + 1) >> 1;
+    if (sh.start[mid] <= lo) bl = mid;
+    else bh = mid - 1;
+  }
+  for (int b = bl; b < B; ++b) {
+    const int st = sh.start[b], en = sh.start[b + 1];
+    if (st >= hi) break;
+    if (en <= lo || en == st) continue;
+    const int blo = max(lo, st) - st, bhi = min(hi, en) - st;
+    run_range<QT, KT, D, GH, NBI, NS>(p, sh, b, blo, bhi, s + b, blo == 0 && bhi == en - st, h0, g);
   }
 }
 
-template <int OT>
-__global__ __launch_bounds__(128) void reduce_kernel(void *out, const float *tmp_out,
-                                                     const float *max_logits,
-                                                     const float *exp_sums,
-                                                     const int32_t *context_lens, int Hq,
-                                                     int D, int max_partitions, int P) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int n = max(context_lens[b], 0);
-  const int np = (n + P - 1) / P;
-  const size_t base = ((size_t)b * Hq + h) * max_partitions;
-  float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, max_logits[base + i]);
-  float W = 0.0f;
-  for (int i = 0; i < np; ++i)
-    W += exp_sums[base + i] * __builtin_amdgcn_exp2f((max_logits[base + i] - M) * kLog2e);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float o = 0.0f;
-    for (int i = 0; i < np; ++i) {
-      const float w =
-          exp_sums[base + i] * __builtin_amdgcn_exp2f((max_logits[base + i] - M) * kLog2e);
-      o = fmaf(w, tmp_out[(base + i) * D + d], o);
+// ---------------------------------------------------------------------------
+// merge of split partials
+// ---------------------------------------------------------------------------
+
+struct ReduceParams {
+  void *out;
+  const float *tmp_out;
+  const float *max_logits;
+  const float *exp_sums;
+  const int32_t *context_lens;
+  int num_seqs;
+  int num_q_heads;
+  int max_partitions;
+  int mode;              // kSplitFixed or kSplitBalanced
+  int partition_blocks;  // fixed
+  int num_splits;        // balanced
+  int skip_single;       // sequences with one piece were written directly
+};
+
+constexpr int kReduceThreads = 256;
+
+// One workgroup per (sequence, run of 256 / D query heads); thread = (head, d).
+template <int OT, int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReduceParams p) {
+  constexpr int HPW = kReduceThreads / D;
+  __shared__ int s_red[2][kReduceThreads / kWave];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int h = blockIdx.y * HPW + tid / D;
+  const int d = tid % D;
+  const int Hq = p.num_q_heads;
+  const int n = p.context_lens[b];
+  const int nblk = num_blocks_of(n);
+
+  int first = 0, np = 0;
+  if (p.mode == kSplitBalanced) {
+    // first block of sequence b and the total, by a workgroup-wide sum
+    int before = 0, all = 0;
+    for (int bb = tid; bb < p.num_seqs; bb += kReduceThreads) {
+      const int c = num_blocks_of(p.context_lens[bb]);
+      all += c;
+      if (bb < b) before += c;
     }
-    store_elem<OT>(out, ((size_t)b * Hq + h) * D + d, np > 0 ? o / W : 0.0f);
+    before = (int)group_sum_i<kWave>(before);
+    all = (int)group_sum_i<kWave>(all);
+    if ((tid & (kWave - 1)) == 0) {
+      s_red[0][tid >> 6] = before;
+      s_red[1][tid >> 6] = all;
+    }
+    __syncthreads();
+    int st = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kReduceThreads / kWave; ++w) {
+      st += s_red[0][w];
+      total += s_red[1][w];
+    }
+    if (nblk > 0) {
+      const long long S = min(p.num_splits, total);
+      // share of block x: the largest s with floor(s * total / S) <= x
+      const int s0 = (int)(((long long)(st + 1) * S - 1) / total);
+      const int s1 = (int)(((long long)(st + nblk) * S - 1) / total);
+      first = s0 + b;
+      np = s1 - s0 + 1;
+    }
+  } else {
+    np = (nblk + p.partition_blocks - 1) / p.partition_blocks;
   }
+  if (h >= Hq) return;
+  const size_t bh = (size_t)b * Hq + h;
+  if (np == 0) {
+    store_elem<OT>(p.out, bh * D + d, 0.0f);
+    return;
+  }
+  if (np == 1 && p.skip_single) return;
+  const size_t base = (p.mode == kSplitBalanced) ? (size_t)h * p.max_partitions + first
+                                                 : bh * p.max_partitions;
+  float M = -INFINITY;
+  for (int i = 0; i < np; ++i) M = fmaxf(M, p.max_logits[base + i]);
+  float W = 0.0f, O = 0.0f;
+  for (int i = 0; i < np; ++i) {
+    const float w = p.exp_sums[base + i] * __builtin_amdgcn_exp2f((p.max_logits[base + i] - M) * kLog2e);
+    W += w;
+    O = fmaf(w, p.tmp_out[(base + i) * D + d], O);
+  }
+  store_elem<OT>(p.out, bh * D + d, O / W);
 }
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <int QT, int KT, int GH>
+constexpr int units_of() {
+  // blocks per unit: two for fp8 caches with up to 4 heads per workgroup
+  // (64 bytes of K and V per lane per block), one otherwise -- two register
+  // stages of one unit each stay within 256 VGPRs
+  return (ElemBytes<KT>::value == 1 && GH <= 4) ? 2 : 1;
+}
+
 
 template <int QT, int KT, int D, int GH>
-hipError_t launch_one(const DecodeParams &p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<QT, KT, D, GH>), grid, dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+const void *kernel_of() {
+  return reinterpret_cast<const void *>(
+      &decode_kernel<QT, KT, D, GH, units_of<QT, KT, GH>(), kStages>);
 }
 
 template <int QT, int KT, int D>
-hipError_t by_gh(int gh, const DecodeParams &p, dim3 grid, hipStream_t s) {
+const void *by_gh(int gh) {
   switch (gh) {
-    case 1: return launch_one<QT, KT, D, 1>(p, grid, s);
-    case 2: return launch_one<QT, KT, D, 2>(p, grid, s);
-    case 4: return launch_one<QT, KT, D, 4>(p, grid, s);
-    case 8: return launch_one<QT, KT, D, 8>(p, grid, s);
+    case 1: return kernel_of<QT, KT, D, 1>();
+    case 2: return kernel_of<QT, KT, D, 2>();
+    case 4: return kernel_of<QT, KT, D, 4>();
+    case 8: return kernel_of<QT, KT, D, 8>();
+    case 16: return kernel_of<QT, KT, D, 16>();
   }
-  return hipErrorInvalidValue;
+  return nullptr;
 }
 
 template <int QT, int KT>
-hipError_t by_d(int d, int gh, const DecodeParams &p, dim3 grid, hipStream_t s) {
+const void *by_d(int d, int gh) {
   switch (d) {
-    case 64: return by_gh<QT, KT, 64>(gh, p, grid, s);
-    case 128: return by_gh<QT, KT, 128>(gh, p, grid, s);
+    case 64: return by_gh<QT, KT, 64>(gh);
+    case 128: return by_gh<QT, KT, 128>(gh);
   }
-  return hipErrorInvalidValue;
+  return nullptr;
+}
+
+const void *decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh) {
+  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return by_d<PA_F32, PA_F32>(d, gh);
+  if (q_dtype == PA_F16 && kv_dtype == PA_F16) return by_d<PA_F16, PA_F16>(d, gh);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return by_d<PA_BF16, PA_BF16>(d, gh);
+  if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN) return by_d<PA_F16, PA_FP8_E4M3FN>(d, gh);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN) return by_d<PA_BF16, PA_FP8_E4M3FN>(d, gh);
+  return nullptr;
 }
 
 }  // namespace
+
+// Workgroups of one decode kernel that fill a device once: compute units x
+// resident workgroups per unit. Looked up once per (device, kernel) and kept
+// for the life of the process (a device property, not state of a call).
+int fill_workgroups(const void *fn) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, fn);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  cache[key] = n;
+  return n;
+}
+
+int balanced_num_splits(const DecodeLaunch &a) {
+  const int gh = heads_per_workgroup(a.num_q_heads / a.num_kv_heads);
+  const void *fn = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh);
+  if (!fn) return 2;
+  const int cus = fill_workgroups(fn);
+  if (cus <= 0) return kMaxAutoSplits / 8;
+  const long long groups = (long long)a.num_kv_heads * (a.num_q_heads / a.num_kv_heads / gh);
+  long long s = ((long long)cus + groups - 1) / groups;
+  if (s < 2) s = 2;
+  if (s > kMaxAutoSplits) s = kMaxAutoSplits;
+  return (int)s;
+}
 
 int launch_decode(const DecodeLaunch &a, void *stream) {
   DecodeParams p;
@@ -485,53 +831,65 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.v_cache = static_cast<const uint8_t *>(a.v_cache);
   p.block_tables = a.block_tables;
   p.context_lens = a.context_lens;
+  p.num_seqs = a.num_seqs;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.mode = a.mode;
+  p.partition_blocks = a.mode == kSplitSingle ? a.max_blocks_per_seq
+                                              : a.partition_size / a.block_size;
   p.max_partitions = a.max_partitions;
-  p.partition_size = a.partition_size;
+  p.num_splits = a.num_splits;
+  p.direct = a.direct;
   p.group = a.num_q_heads / a.num_kv_heads;
   const float ks = a.kv_dtype == PA_FP8_E4M3FN ? a.k_scale : 1.0f;
   p.scale_log2 = a.scale * ks * kLog2e;
   p.v_scale = a.kv_dtype == PA_FP8_E4M3FN ? a.v_scale : 1.0f;
   const int gh = heads_per_workgroup(p.group);
-  const int parts = a.partition_size > 0 ? a.max_partitions : 1;
-  const dim3 grid(parts, a.num_kv_heads * (p.group / gh), a.num_seqs);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipErrorInvalidValue;
-  if (a.q_dtype == PA_F32 && a.kv_dtype == PA_F32) e = by_d<PA_F32, PA_F32>(a.head_dim, gh, p, grid, s);
-  else if (a.q_dtype == PA_F16 && a.kv_dtype == PA_F16) e = by_d<PA_F16, PA_F16>(a.head_dim, gh, p, grid, s);
-  else if (a.q_dtype == PA_BF16 && a.kv_dtype == PA_BF16) e = by_d<PA_BF16, PA_BF16>(a.head_dim, gh, p, grid, s);
-  else if (a.q_dtype == PA_F16 && a.kv_dtype == PA_FP8_E4M3FN) e = by_d<PA_F16, PA_FP8_E4M3FN>(a.head_dim, gh, p, grid, s);
-  else if (a.q_dtype == PA_BF16 && a.kv_dtype == PA_FP8_E4M3FN) e = by_d<PA_BF16, PA_FP8_E4M3FN>(a.head_dim, gh, p, grid, s);
-  return (int)e;
+  const void *fn = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh);
+  if (!fn) return (int)hipErrorInvalidValue;
+  const int head_groups = a.num_kv_heads * (p.group / gh);
+  dim3 grid;
+  if (a.mode == kSplitBalanced) grid = dim3(a.num_splits, head_groups, 1);
+  else if (a.mode == kSplitFixed) grid = dim3(a.max_partitions, head_groups, a.num_seqs);
+  else grid = dim3(1, head_groups, a.num_seqs);
+  void *args[] = {&p};
+  hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), args, 0,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return (int)e;
+  return (int)hipGetLastError();
 }
 
-int launch_reduce(void *out, const float *tmp_out, const float *max_logits, const float *exp_sums,
-                  const int32_t *context_lens, int num_seqs, int num_q_heads, int head_dim,
-                  int max_partitions, int partition_size, int out_dtype, void *stream) {
-  const dim3 grid(num_q_heads, num_seqs);
+int launch_reduce(const ReduceLaunch &a, void *stream) {
+  ReduceParams p;
+  p.out = a.out;
+  p.tmp_out = a.tmp_out;
+  p.max_logits = a.max_logits;
+  p.exp_sums = a.exp_sums;
+  p.context_lens = a.context_lens;
+  p.num_seqs = a.num_seqs;
+  p.num_q_heads = a.num_q_heads;
+  p.max_partitions = a.max_partitions;
+  p.mode = a.mode;
+  p.partition_blocks = a.mode == kSplitFixed ? a.partition_size / a.block_size : 0;
+  p.num_splits = a.num_splits;
+  p.skip_single = a.skip_single;
+  const int hpw = kReduceThreads / a.head_dim;
+  const dim3 grid(a.num_seqs, (a.num_q_heads + hpw - 1) / hpw);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (out_dtype) {
-    case PA_F32:
-      hipLaunchKernelGGL(reduce_kernel<PA_F32>, grid, dim3(128), 0, s, out, tmp_out, max_logits,
-                         exp_sums, context_lens, num_q_heads, head_dim, max_partitions,
-                         partition_size);
-      break;
-    case PA_F16:
-      hipLaunchKernelGGL(reduce_kernel<PA_F16>, grid, dim3(128), 0, s, out, tmp_out, max_logits,
-                         exp_sums, context_lens, num_q_heads, head_dim, max_partitions,
-                         partition_size);
-      break;
-    case PA_BF16:
-      hipLaunchKernelGGL(reduce_kernel<PA_BF16>, grid, dim3(128), 0, s, out, tmp_out, max_logits,
-                         exp_sums, context_lens, num_q_heads, head_dim, max_partitions,
-                         partition_size);
-      break;
-    default:
-      return (int)hipErrorInvalidValue;
+#define PA_RED(OT, D)                                                                          \
+  if (a.out_dtype == OT && a.head_dim == D) {                                                  \
+    hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(kReduceThreads), 0, s, p);          \
+    return (int)hipGetLastError();                                                             \
   }
-  return (int)hipGetLastError();
+  PA_RED(PA_F32, 64)
+  PA_RED(PA_F32, 128)
+  PA_RED(PA_F16, 64)
+  PA_RED(PA_F16, 128)
+  PA_RED(PA_BF16, 64)
+  PA_RED(PA_BF16, 128)
+#undef PA_RED
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -113,6 +113,14 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Integer sum over aligned groups of N lanes.
+template <int N>
+__device__ __forceinline__ int group_sum_i(int v) {
+#pragma unroll
+  for (int off = 1; off < N; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 template <int N>
 __device__ __forceinline__ float group_max(float v) {
   if constexpr (N >= 2) v = fmaxf(v, dpp<kDppQuadXor1>(v));

@@ -7,12 +7,28 @@
 
 namespace pa {
 
+// How a decode cuts each sequence's context into the ranges one workgroup
+// reads.
+enum SplitMode : int {
+  kSplitSingle = 0,    // one range per sequence
+  kSplitFixed = 1,     // fixed partitions of partition_size tokens
+  kSplitBalanced = 2,  // all sequences' blocks end to end, cut into num_splits equal shares
+};
+
+// Balanced split: at most this many sequences per call (the per-sequence
+// start blocks live in LDS), and at most this many shares.
+constexpr int kMaxBalancedSeqs = 1024;
+constexpr int kMaxAutoSplits = 2048;
+
 struct DecodeLaunch {
-  // outputs: single pass writes `out`; split writes the three partial arrays
+  // outputs: `out`, and/or the three partial arrays
   void *out;
   float *tmp_out;
   float *max_logits;
   float *exp_sums;
+  // partial-array stride: fixed split, per (sequence, head) -- index
+  // ((b * Hq + h) * max_partitions + partition); balanced split, per head --
+  // index (h * max_partitions + share + b), max_partitions = num_splits + B
   int max_partitions;
   // inputs
   const void *q;
@@ -23,15 +39,30 @@ struct DecodeLaunch {
   int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   float scale, k_scale, v_scale;
   int q_dtype, kv_dtype;
-  int partition_size;  // 0 = single pass
+  int mode;            // SplitMode
+  int partition_size;  // fixed split: tokens per partition
+  int num_splits;      // balanced split: shares
+  int direct;          // a range covering a whole sequence writes `out` directly
+};
+
+struct ReduceLaunch {
+  void *out;
+  const float *tmp_out;
+  const float *max_logits;
+  const float *exp_sums;
+  const int32_t *context_lens;
+  int num_seqs, num_q_heads, head_dim, block_size;
+  int max_partitions;
+  int mode;            // kSplitFixed or kSplitBalanced
+  int partition_size;  // fixed
+  int num_splits;      // balanced
+  int skip_single;     // sequences held in one piece were already written
+  int out_dtype;
 };
 
 // Each returns 0 on success or the runtime's error code.
 int launch_decode(const DecodeLaunch &a, void *stream);
-int launch_reduce(void *out, const float *tmp_out, const float *max_logits,
-                  const float *exp_sums, const int32_t *context_lens, int num_seqs,
-                  int num_q_heads, int head_dim, int max_partitions, int partition_size,
-                  int out_dtype, void *stream);
+int launch_reduce(const ReduceLaunch &a, void *stream);
 int launch_reshape_and_cache(const void *key, const void *value, void *k_cache, void *v_cache,
                              const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
                              int head_dim, int src_dtype, int cache_dtype, float k_scale,
@@ -39,9 +70,13 @@ int launch_reshape_and_cache(const void *key, const void *value, void *k_cache, 
 int launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
                        int num_pairs, size_t block_bytes, void *stream);
 
-// heads of one KV group that one workgroup serves (a divisor of the group, <= 8)
+// Shares a balanced split uses on the current device: enough workgroups to
+// fill every compute unit once at the decode kernel's occupancy.
+int balanced_num_splits(const DecodeLaunch &a);
+
+// heads of one KV group that one workgroup serves (a divisor of the group, <= 16)
 inline int heads_per_workgroup(int group) {
-  return group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  return group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
 }
 
 }  // namespace pa

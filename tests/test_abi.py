@@ -57,6 +57,9 @@ def test_workspace_size():
     # B * Hq * NP * (d + 2) * 4
     assert pa.decode_workspace_size(32, 32, 128, 256, 16, 256) == 32 * 32 * 16 * 130 * 4
     assert pa.decode_workspace_size(32, 32, 128, 256, 16, 0) == 0
+    # balanced split: Hq * (S + B) * (d + 2) * 4, S = 2048 for the automatic choice
+    assert pa.decode_workspace_size(32, 32, 128, 256, 16, -64) == 32 * (64 + 32) * 130 * 4
+    assert pa.decode_workspace_size(32, 32, 128, 256, 16, -1) == 32 * (2048 + 32) * 130 * 4
 
 
 def _decode(**kw):
@@ -79,9 +82,13 @@ def _decode(**kw):
     (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),  # fp8 cache needs a 16-bit query
     (dict(qt=7), 3),
     (dict(P=24), 2),                               # not a multiple of block_size
-    (dict(P=-16), 2),
     (dict(P=16), 1),                               # split without workspace
     (dict(P=16, ws=FAKE, wsb=10), 4),              # workspace too small
+    (dict(P=-1), 1),                               # balanced split without workspace
+    (dict(P=-4, ws=FAKE, wsb=10), 4),
+    (dict(P=-1, ws=FAKE, wsb=10), 4),
+    (dict(P=-1, B=1025), 3),                       # balanced split: at most 1024 sequences
+    (dict(P=-4096), 3),                            # at most 2048 shares
     (dict(scale=float("nan")), 2),
     (dict(qt=pa.PA_BF16, kt=pa.PA_FP8_E4M3FN, ks=float("inf")), 2),
     (dict(Hq=65536 * 8, Hkv=65536), 3),            # launch grid limit

@@ -41,14 +41,15 @@ def test_tiny_fp32_gqa2():
 
 @pytest.mark.parametrize("q_dtype,kv_dtype", PAIRS)
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("P", [0, 16, 256])
+@pytest.mark.parametrize("P", [0, 16, 256, -1, -5])
 def test_edge_lengths(q_dtype, kv_dtype, d, P):
-    wl = W.custom(EDGE_CTX, 8, 2, d, q_dtype=q_dtype, kv_dtype=kv_dtype, seed=d + P)
+    wl = W.custom(EDGE_CTX, 8, 2, d, q_dtype=q_dtype, kv_dtype=kv_dtype, seed=d + abs(P))
     _check(wl, P, f"{q_dtype}/{kv_dtype} d={d} P={P}")
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (12, 4), (16, 2), (16, 1), (32, 2)])
-@pytest.mark.parametrize("P", [0, 64])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (12, 4), (16, 2), (16, 1), (32, 2),
+                                    (32, 1)])
+@pytest.mark.parametrize("P", [0, 64, -1, -3])
 def test_gqa_groups(Hq, Hkv, P):
     wl = W.custom([5, 100, 700], Hq, Hkv, 128, q_dtype="bf16", kv_dtype="bf16", seed=Hq * Hkv)
     _check(wl, P, f"Hq={Hq} Hkv={Hkv} P={P}")
@@ -56,14 +57,14 @@ def test_gqa_groups(Hq, Hkv, P):
 
 def test_zero_context_gives_zeros():
     wl = W.custom([0, 40, 0, 3], 4, 2, 64, q_dtype="bf16", kv_dtype="bf16", seed=1)
-    for P in (0, 16):
+    for P in (0, 16, -1, -3):
         _check(wl, P, f"zero ctx P={P}")
         d, out = device_step(wl, P)
         o = W.widen_to_f64(out)
         assert (o[0] == 0).all() and (o[2] == 0).all()
 
 
-@pytest.mark.parametrize("P", [0, 32])
+@pytest.mark.parametrize("P", [0, 32, -1, -4])
 def test_poisoned_unused_slots_are_never_read(P):
     """Unused block-table entries point at a NaN-filled block and the unused
     tail of every last block is NaN: the output is finite and bitwise equal to
@@ -96,7 +97,7 @@ def test_poisoned_unused_slots_are_never_read(P):
     assert torch.equal(out_dirty, out_clean)
 
 
-@pytest.mark.parametrize("P", [0, 64])
+@pytest.mark.parametrize("P", [0, 64, -1, -6])
 def test_physical_relabelling_is_bitwise_invariant(P):
     wl = W.custom([300, 17, 1000, 64], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", seed=9,
                   extra_blocks=20)
@@ -113,7 +114,7 @@ def test_aliased_blocks_equal_private_copies_bitwise():
                    new_key=None, new_value=None, new_slots=None)
     private = W.unshare(done)
     assert private.num_blocks > done.num_blocks
-    for P in (0, 32):
+    for P in (0, 32, -1, -5):
         _, a = device_step(done, P)
         _, b = device_step(private, P)
         assert torch.equal(a, b)
@@ -132,7 +133,7 @@ def test_deterministic():
     wl = W.custom([2000, 333, 4096], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", seed=4)
     d = device_inputs(wl)
     device_writes(wl, d)
-    for P in (0, 256):
+    for P in (0, 256, -1, -7):
         a = device_decode(wl, d, P)
         b = device_decode(wl, d, P)
         assert torch.equal(a, b)
@@ -143,7 +144,7 @@ def test_partition_size_independence():
     d = device_inputs(wl)
     device_writes(wl, d)
     base = W.widen_to_f64(device_decode(wl, d, 0))
-    for P in (16, 48, 256, 1024, 4096):
+    for P in (16, 48, 256, 1024, 4096, -1, -2, -9, -2048):
         other = W.widen_to_f64(device_decode(wl, d, P))
         assert np.abs(other - base).max() <= 1e-5
 
@@ -189,3 +190,65 @@ def test_fp8_decode_widening_covers_every_code():
     expect = oracle.e4m3fn_decode(row)
     for h in range(4):
         assert np.array_equal(got[h], expect[h // 2])
+
+
+def test_zero_context_balanced_only_zeros():
+    """Every sequence empty: no share has work, the merge writes zeros."""
+    wl = W.custom([0, 0, 0], 8, 2, 128, q_dtype="bf16", kv_dtype="bf16", seed=2)
+    d = device_inputs(wl)
+    for P in (-1, -3):
+        out = device_decode(wl, d, P)
+        assert (W.widen_to_f64(out) == 0).all()
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 5, 64, 2048])
+def test_balanced_more_shares_than_blocks(S):
+    """Shares are clamped to the number of blocks; short and empty sequences."""
+    wl = W.custom([1, 2, 0, 17, 16], 8, 4, 64, q_dtype="f16", kv_dtype="f16", seed=S)
+    _check(wl, -S, f"balanced S={S}")
+
+
+def test_balanced_many_sequences():
+    rng = np.random.default_rng(3)
+    ctx = rng.integers(0, 80, size=1024)
+    wl = W.custom(ctx, 8, 2, 64, q_dtype="bf16", kv_dtype="bf16", seed=3)
+    _check(wl, -1, "balanced 1024 seqs")
+    wl = W.custom(ctx[:1000].tolist() + [5000] + ctx[1000:].tolist(), 4, 1, 128,
+                  q_dtype="bf16", kv_dtype="fp8_e4m3fn", seed=4)
+    with pytest.raises(pa.PaError, match="not supported"):
+        device_step(wl, -1)
+    _check(wl, 256, "1025 seqs, fixed split")
+
+
+@pytest.mark.parametrize("S", [1, 7, 100])
+def test_balanced_long_single_sequence(S):
+    wl = W.custom([30000], 32, 8, 128, q_dtype="bf16", kv_dtype="fp8_e4m3fn", seed=S)
+    _check(wl, -S, f"one 30000-token sequence, S={S}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("S", [2, 5, 33])
+def test_balanced_partials_against_oracle(kv_dtype, S):
+    """Each balanced-split piece (share s, sequence b) lands in column s + b
+    with the oracle's statistics; the merge gives the oracle's merge."""
+    wl = W.custom([1, 95, 0, 96, 97, 400], 8, 2, 128, q_dtype="bf16", kv_dtype=kv_dtype,
+                  seed=13 + S)
+    kc, vc, _ = oracle_step(wl, decode=False)
+    pieces = oracle.balanced_pieces(wl.context_lens, 16, S)
+    m, l, o = oracle.paged_decode_pieces(wl.q, kc, vc, wl.block_tables, wl.context_lens,
+                                         wl.scale, pieces, wl.k_scale, wl.v_scale)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    tmp, mx, es = pa.decode_partials(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], -S, scale=wl.scale, k_scale=wl.k_scale,
+                                     v_scale=wl.v_scale)
+    assert tmp.shape == (8, S + 6, 128)
+    tmp_n, mx_n, es_n = (t.cpu().double().numpy() for t in (tmp, mx, es))
+    for i, (s, b, _, _) in enumerate(pieces):
+        col = s + b
+        assert np.abs(mx_n[:, col] - m[i]).max() <= 1e-4 * (1 + np.abs(m[i]).max())
+        assert np.allclose(es_n[:, col], l[i], rtol=1e-4, atol=1e-5)
+        assert np.allclose(tmp_n[:, col], o[i], rtol=1e-3, atol=1e-4)
+    out = pa.decode_reduce(tmp, mx, es, d["context_lens"], -S, out_dtype=torch.float32)
+    ref = oracle.reduce_pieces(m, l, o, pieces, wl.num_seqs)
+    assert np.abs(out.cpu().double().numpy() - ref).max() <= 1e-4

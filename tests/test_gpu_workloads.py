@@ -31,24 +31,25 @@ def _run(wl, partition_size=None, seqs=None, full_pool=True):
 
 def test_llama3_8b_b32():
     wl = W.build("llama3_8b_b32")
-    for P in (wl.partition_size, 0, 512):
+    for P in (wl.partition_size, 0, 256, 512):
         _run(wl, P)
 
 
 def test_mha_b32_ctx4096():
     wl = W.build("mha_b32_ctx4096")
-    for P in (wl.partition_size, 512):
+    for P in (wl.partition_size, 0, 512):
         _run(wl, P, seqs=[0, 17, 31])
 
 
 def test_shared_prefix_cow_b64():
     wl = W.build("shared_prefix_cow_b64")
     assert len(wl.cow_pairs) == 48
-    for P in (wl.partition_size, 0):
+    for P in (wl.partition_size, 0, 256):
         _run(wl, P)
 
 
 def test_long_ctx_fp8_b8():
     wl = W.build("long_ctx_fp8_b8")
     seqs = [int(np.argmin(wl.context_lens)), int(np.argmax(wl.context_lens))]
-    _run(wl, None, seqs=seqs, full_pool=False)
+    for P in (wl.partition_size, -1):
+        _run(wl, P, seqs=seqs, full_pool=False)

@@ -26,8 +26,9 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import (e4m3fn_decode, e4m3fn_encode, paged_decode, paged_decode_partials,
-                    reduce_partials, to_f64)
+from oracle import (balanced_pieces, e4m3fn_decode, e4m3fn_encode, paged_decode,
+                    paged_decode_partials, paged_decode_pieces, reduce_partials, reduce_pieces,
+                    to_f64)
 
 
 def _scatter(logical_k, logical_v, physical_ids, bs, num_blocks, rng):
@@ -256,6 +257,53 @@ def test_split_partials_brute_force():
             assert l[0, h, p] == pytest.approx(sum(e), abs=1e-12)
             ref = sum(ei * V[0][lo + j, 0] for j, ei in enumerate(e)) / sum(e)
             np.testing.assert_allclose(o[0, h, p], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("ctx,S", [([1, 47, 0, 48, 49, 200], 3), ([1, 47, 0, 48, 49, 200], 7),
+                                   ([5], 4), ([0, 0], 3), ([16, 1, 2], 64), ([200, 17], 2)])
+def test_balanced_pieces_tile_every_sequence(ctx, S):
+    """Brute force over blocks: every block of every sequence lies in exactly
+    one piece, pieces of a share are consecutive, and shares differ in size
+    by at most one block."""
+    bs = 4
+    pieces = balanced_pieces(ctx, bs, S)
+    owner = {}
+    for s, b, fb, eb in pieces:
+        assert 0 <= fb < eb <= -(-ctx[b] // bs)
+        for j in range(fb, eb):
+            assert (b, j) not in owner
+            owner[(b, j)] = s
+    every = [(b, j) for b, n in enumerate(ctx) for j in range(-(-n // bs))]
+    assert sorted(owner) == sorted(every)
+    # logical order of the concatenation is non-decreasing in share
+    shares = [owner[k] for k in every]
+    assert shares == sorted(shares)
+    sizes = np.bincount(shares) if shares else np.zeros(0, int)
+    if len(every):
+        assert len(sizes) == min(S, len(every)) and sizes.max() - sizes.min() <= 1
+
+
+@pytest.mark.parametrize("S", [2, 3, 5, 64])
+def test_balanced_split_identity(S):
+    """Merging the balanced pieces gives dense attention (float64), and each
+    piece's statistics are those of its own token slice (brute force)."""
+    rng = np.random.default_rng(S)
+    ctx = [1, 47, 0, 48, 49, 200]
+    q, K, V, kc, vc, table, cl = _random_case(rng, ctx, 4, 2, 16, 4)
+    dense = paged_decode(q, kc, vc, table, cl, 0.2)
+    pieces = balanced_pieces(cl, 4, S)
+    m, l, o = paged_decode_pieces(q, kc, vc, table, cl, 0.2, pieces)
+    np.testing.assert_allclose(reduce_pieces(m, l, o, pieces, len(ctx)), dense, rtol=0,
+                               atol=1e-12)
+    for i, (s, b, fb, eb) in enumerate(pieces):
+        lo, hi = fb * 4, min(eb * 4, ctx[b])
+        for h in range(4):
+            sc = [float(np.float32(0.2)) * float(np.dot(q[b, h], K[b][j, h // 2]))
+                  for j in range(lo, hi)]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            assert m[i, h] == pytest.approx(mx, abs=1e-12)
+            assert l[i, h] == pytest.approx(sum(e), abs=1e-12)
 
 
 def test_fp8_cache_is_attention_over_dequantised_values():

@@ -77,7 +77,8 @@ class Workload:
     new_key: Optional[np.ndarray] = None      # [B, Hkv, d] (q dtype)
     new_value: Optional[np.ndarray] = None
     new_slots: Optional[np.ndarray] = None    # [B] int64
-    partition_size: int = 0                   # launch configuration, 0 = single pass
+    partition_size: int = 0                   # launch configuration: 0 single pass, >0 tokens
+                                              # per partition, <0 balanced split (-1: automatic)
     info: Dict = field(default_factory=dict)
 
     @property
@@ -170,7 +171,7 @@ def tiny_fp32_gqa2(seed: int = 1, partition_size: int = 0) -> Workload:
                            "f32", "f32", partition_size)
 
 
-def llama3_8b_b32(seed: int = 2, partition_size: int = 256) -> Workload:
+def llama3_8b_b32(seed: int = 2, partition_size: int = -1) -> Workload:
     """Llama-3-8B-shaped layer: batch 32, context lengths uniform on
     [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16, block_size 16,
     pool 10 % larger than the blocks in use, handed out in random order."""
@@ -182,7 +183,7 @@ def llama3_8b_b32(seed: int = 2, partition_size: int = 256) -> Workload:
                            "bf16", "bf16", partition_size, mbs=4096 // 16)
 
 
-def mha_b32_ctx4096(seed: int = 3, partition_size: int = 0) -> Workload:
+def mha_b32_ctx4096(seed: int = 3, partition_size: int = -1) -> Workload:
     """MHA-shaped layer: batch 32, every context 4096 tokens, 32 query = 32 KV
     heads, head_dim 128, fp16 (2 GiB of K+V), block_size 16, pool exactly the
     8192 blocks in use, handed out in random order."""
@@ -192,7 +193,7 @@ def mha_b32_ctx4096(seed: int = 3, partition_size: int = 0) -> Workload:
                            "f16", "f16", partition_size)
 
 
-def shared_prefix_cow_b64(seed: int = 4, partition_size: int = 256, groups: int = 16,
+def shared_prefix_cow_b64(seed: int = 4, partition_size: int = -1, groups: int = 16,
                           samples: int = 4, prompt: int = 2048, parent_decoded: int = 8,
                           private: int = 128, Hq: int = 32, Hkv: int = 8, d: int = 128,
                           bs: int = 16) -> Workload:
