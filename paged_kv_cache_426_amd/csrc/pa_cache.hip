@@ -33,16 +33,25 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
   constexpr int CB = ElemBytes<CT>::value;
   constexpr int VEC = 16 / SB;  // source elements per 16-byte piece
   const int t = blockIdx.x;
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
   const bool is_v = blockIdx.y == 1;
   const uint8_t *src = (is_v ? value : key) + (size_t)t * row_elems * SB;
-  uint8_t *dst = (is_v ? v_cache : k_cache) + (size_t)slot * row_elems * CB;
   const int pieces = row_elems / VEC;
   if constexpr (ST == CT) {
-    for (int i = threadIdx.x; i < pieces; i += kCopyThreads)
+    // the first piece of the row is loaded together with the slot (one
+    // memory round trip instead of two for rows of up to 4 KiB)
+    const int i0 = threadIdx.x;
+    u32x4 first = {0u, 0u, 0u, 0u};
+    if (i0 < pieces) first = reinterpret_cast<const u32x4 *>(src)[i0];
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) return;
+    uint8_t *dst = (is_v ? v_cache : k_cache) + (size_t)slot * row_elems * CB;
+    if (i0 < pieces) reinterpret_cast<u32x4 *>(dst)[i0] = first;
+    for (int i = i0 + kCopyThreads; i < pieces; i += kCopyThreads)
       reinterpret_cast<u32x4 *>(dst)[i] = reinterpret_cast<const u32x4 *>(src)[i];
   } else {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) return;
+    uint8_t *dst = (is_v ? v_cache : k_cache) + (size_t)slot * row_elems * CB;
     static_assert(CT == PA_FP8_E4M3FN, "only fp8 quantisation converts");
     const float scale = is_v ? v_scale : k_scale;
     for (int i = threadIdx.x; i < pieces; i += kCopyThreads) {

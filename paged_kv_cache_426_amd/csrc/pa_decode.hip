@@ -719,13 +719,48 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
   if (np == 1 && p.skip_single) return;
   const size_t base = (p.mode == kSplitBalanced) ? (size_t)h * p.max_partitions + first
                                                  : bh * p.max_partitions;
+  // Pieces are read R at a time, every load of a batch issued before any is
+  // used, so that a sequence of at most R pieces costs one memory round trip
+  // (the first batch is loaded whole and kept for the weighted sum).
+  constexpr int R = 8;
+  float mm[R], ll[R], tt[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (u < np) {
+      mm[u] = p.max_logits[base + u];
+      ll[u] = p.exp_sums[base + u];
+      tt[u] = p.tmp_out[(base + u) * D + d];
+    }
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, p.max_logits[base + i]);
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+    if (u < np) M = fmaxf(M, mm[u]);
+  for (int i0 = R; i0 < np; i0 += R) {
+    float mx[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) mx[u] = i0 + u < np ? p.max_logits[base + i0 + u] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < R; ++u) M = fmaxf(M, mx[u]);
+  }
+  // weights w_p = l_p exp(m_p - M), summed in piece order
   float W = 0.0f, O = 0.0f;
-  for (int i = 0; i < np; ++i) {
-    const float w = p.exp_sums[base + i] * __builtin_amdgcn_exp2f((p.max_logits[base + i] - M) * kLog2e);
-    W += w;
-    O = fmaf(w, p.tmp_out[(base + i) * D + d], O);
+  for (int i0 = 0; i0 < np; i0 += R) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (i0 + u < np) {
+          mm[u] = p.max_logits[base + i0 + u];
+          ll[u] = p.exp_sums[base + i0 + u];
+          tt[u] = p.tmp_out[(base + i0 + u) * D + d];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      if (i0 + u < np) {
+        const float w = ll[u] * __builtin_amdgcn_exp2f((mm[u] - M) * kLog2e);
+        W += w;
+        O = fmaf(w, tt[u], O);
+      }
   }
   store_elem<OT>(p.out, bh * D + d, O / W);
 }

@@ -252,3 +252,58 @@ def test_balanced_partials_against_oracle(kv_dtype, S):
     out = pa.decode_reduce(tmp, mx, es, d["context_lens"], -S, out_dtype=torch.float32)
     ref = oracle.reduce_pieces(m, l, o, pieces, wl.num_seqs)
     assert np.abs(out.cpu().double().numpy() - ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("P", [-1, -3, 16, 64])
+def test_split_decode_ignores_workspace_contents(P):
+    """Whatever the split decode's workspace held before (zeros, all ones,
+    random bytes, or a previous call's partials) the output is bitwise the
+    same and matches the oracle."""
+    wl = W.custom([1, 300, 17, 0, 1000, 64], 16, 4, 128, q_dtype="bf16", kv_dtype="bf16", seed=21)
+    kc, vc, ref = oracle_step(wl)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    B, Hq, dd = wl.q.shape
+    need = pa.decode_workspace_size(B, Hq, dd, wl.max_blocks_per_seq, 16, P)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    for fill in ("zero", "ones", "random", "reuse", "reuse"):
+        if fill == "zero":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(255)
+        elif fill == "random":
+            ws.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen))
+        out = pa.decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                        scale=wl.scale, partition_size=P, workspace=ws)
+        outs.append(out.clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    assert_close(W.widen_to_f64(outs[0]), ref, "bf16", f"workspace contents P={P}")
+
+
+@pytest.mark.parametrize("P", [-5, 32])
+def test_decode_equals_partials_then_reduce(P):
+    """pa_decode equals the two public stages it is made of (partials, then
+    the merge) bit for bit for the sequences that are split (1 and 3 here,
+    under both splits); a sequence held in one piece is written directly by
+    pa_decode, without the merge's w * o / w round trip, so it may differ in
+    the last place."""
+    wl = W.custom([5, 200, 1, 777], 8, 2, 64, q_dtype="f16", kv_dtype="f16", seed=22)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    whole = device_decode(wl, d, P)
+    tmp, mx, es = pa.decode_partials(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], P, scale=wl.scale)
+    sep = pa.decode_reduce(tmp, mx, es, d["context_lens"], P, out_dtype=torch.float16)
+    assert torch.equal(whole[[1, 3]], sep[[1, 3]])
+    torch.testing.assert_close(whole, sep, rtol=2e-3, atol=1e-5)
+
+
+def test_merge_many_pieces():
+    """Long sequences split into many pieces (up to 64 per sequence) merge
+    correctly."""
+    wl = W.custom([16384, 9000, 3], 32, 8, 128, q_dtype="bf16", kv_dtype="fp8_e4m3fn", seed=23)
+    for P in (256, -400):
+        _check(wl, P, f"many pieces P={P}")
