@@ -58,8 +58,10 @@ namespace {
 
 constexpr int kBs = 16;  // tokens per cache block
 constexpr int kStages = 2;  // register stages of the load pipeline
-constexpr int kWaves = 2;  // waves per workgroup
-constexpr int kThreads = kWaves * kWave;
+// Waves per workgroup (NW below): a fixed partition or a single sequence is
+// split between kFixedWaves waves; a balanced split runs one wide workgroup
+// per compute unit where the registers allow (see balanced_waves).
+constexpr int kFixedWaves = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -271,17 +273,18 @@ __device__ __forceinline__ void wave_lds_fence() {
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 
-template <int QT, int KT, int D, int GH, int NBI>
+template <int QT, int KT, int D, int GH, int NBI, int NW>
 struct Shared {
-  float p[kWaves][NBI * kBs][GH];   // probabilities of the current unit
-  float alpha[kWaves][GH];          // rescale factor of the current unit
-  float m[kWaves][GH];              // per-wave softmax state at the end of a range
-  float l[kWaves][GH];
-  float acc[kWaves][GH][D];
+  float p[NW][NBI * kBs][GH];   // probabilities of the current unit
+  float alpha[NW][GH];          // rescale factor of the current unit
+  float m[NW][GH];              // per-wave softmax state at the end of a range
+  float l[NW][GH];
+  float acc[NW][GH][D];
   // K tiles of the current unit, one per wave and block
-  uint8_t kt[kWaves][NBI][kBs * (D * ElemBytes<KT>::value + 16)] __attribute__((aligned(16)));
+  uint8_t kt[NW][NBI][kBs * (D * ElemBytes<KT>::value + 16)] __attribute__((aligned(16)));
   int start[kMaxBalancedSeqs + 1];  // balanced split: first block of each sequence
-  int wave_sum[kWaves];
+  int ctx[kMaxBalancedSeqs];        // balanced split: context length of each sequence
+  int wave_sum[NW];
 };
 
 template <int QT, int KT, int D, int GH, int NBI>
@@ -291,15 +294,65 @@ struct Stage {
   VPiece<KT> v[NBI][G::nvl];
 };
 
-// One range [blo, bhi) of the blocks of sequence b, all waves.
-template <int QT, int KT, int D, int GH, int NBI, int NS>
-__device__ __forceinline__ void run_range(const DecodeParams &p,
-                                          Shared<QT, KT, D, GH, NBI> &sh, int b, int blo,
-                                          int bhi, int piece, bool whole, int h0, int g) {
+// A range is the blocks [blo, bhi) of sequence b, written as partial
+// `piece` (or to `out` when it is the whole sequence). The units of all
+// ranges of a workgroup are dealt to its waves in turn, counting on across
+// ranges (so the waves' shares of the work differ by one unit at most); a
+// segment is up to kIdsUnits of a wave's units of one range (chunk c), the
+// span one register of block ids covers.
+// A workgroup's work item: the query heads h0 .. h0 + GH - 1 (KV head g)
+// over one balanced share (blocks [lo, hi) of all sequences end to end), or
+// over a single range in the other modes.
+struct Item {
+  int h0, g;
+  int share, lo, hi;
+};
+
+struct Seg {
+  int item;   // work item of the range
+  int h0, g;  // its query heads and KV head
+  int share, ihi;  // balanced: its share and the share's end block
+  int b, blo, bhi, piece;
+  int n;      // context length of sequence b
+  int whole;  // the range is the whole sequence
+  int u0;     // units of the workgroup's earlier ranges
+  int w0;     // this wave's first unit of the range
+  int c;      // chunk of the range
+  int nk;     // this wave's units in the range
+  int kn;     // this wave's units in this segment
+  int last;   // last segment of its range: the range's epilogue follows it
+  int valid;
+};
+
+// The sequence holding block x of the blocks end to end (the largest b with
+// start[b] <= x; it holds blocks since start[b + 1] > x).
+template <class Sh>
+__device__ __forceinline__ int first_seq_of(const Sh &sh, int B, int x) {
+  int bl = 0, bh = B - 1;
+  while (bl < bh) {
+    const int mid = (bl + bh + 1) >> 1;
+    if (sh.start[mid] <= x) bl = mid;
+    else bh = mid - 1;
+  }
+  return bl;
+}
+
+// All ranges of a workgroup's work items (one range, or the ranges of one
+// or two balanced shares), all waves. The segments of a wave form one
+// pipelined stream: while the last units of a segment are computed, the
+// first unit of the next segment is already being loaded (its block ids and
+// query fragments were fetched one segment ahead), so a switch between
+// ranges costs only the epilogue of the finished range.
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW>
+__device__ __forceinline__ void run_ranges(const DecodeParams &p,
+                                           Shared<QT, KT, D, GH, NBI, NW> &sh, const Item (&items)[2],
+                                           int n_items, int b_first, int n_first, int blo_first,
+                                           int bhi_first, int piece_first, bool whole_first) {
   using G = Geo<QT, KT, D>;
   using QOp = typename QOpT<QT>::type;
   using St = Stage<QT, KT, D, GH, NBI>;
   constexpr int QB = ElemBytes<QT>::value;
+  constexpr int kIdsUnits = kWave / NBI;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -308,17 +361,82 @@ __device__ __forceinline__ void run_range(const DecodeParams &p,
   const int tl = lane & 15;  // MFMA column: token within a block
   const int r = lane / G::lpt;  // V layout: token row within a load
   const int c = lane % G::lpt;  // V layout: 8-element column group
-  b = uniform(b);
-  blo = uniform(blo);
-  bhi = uniform(bhi);
-  const int n = uniform(p.context_lens[b]);
-  const int tok_lim = min(bhi * kBs, n);
-  const int nunits = (bhi - blo + NBI - 1) / NBI;
   const int Hq = p.num_q_heads;
+  const int B = p.num_seqs;
+  const bool balanced = p.mode == kSplitBalanced;
 
-  // query fragments (A operand): row tl holds head h0 + tl % GH
-  QOp qa[G::ksteps];
-  {
+  // ---- segments ------------------------------------------------------------
+  auto make_seg = [&](int item, const Item &it, int b, int n, int blo, int bhi, int piece,
+                      bool whole, int u0, int ch) {
+    Seg sg;
+    sg.item = item;
+    sg.h0 = it.h0;
+    sg.g = it.g;
+    sg.share = it.share;
+    sg.ihi = it.hi;
+    sg.b = b;
+    sg.n = n;
+    sg.blo = blo;
+    sg.bhi = bhi;
+    sg.piece = piece;
+    sg.whole = whole;
+    sg.u0 = u0;
+    sg.w0 = (wave - u0 % NW + NW) % NW;
+    sg.c = ch;
+    const int nunits = (bhi - blo + NBI - 1) / NBI;
+    sg.nk = sg.w0 < nunits ? (nunits - sg.w0 + NW - 1) / NW : 0;
+    const int nchunks = max(1, (sg.nk + kIdsUnits - 1) / kIdsUnits);
+    sg.kn = max(0, min(kIdsUnits, sg.nk - ch * kIdsUnits));
+    sg.last = ch == nchunks - 1;
+    sg.valid = 1;
+    return sg;
+  };
+  // first chunk of the range of sequence b within balanced item it
+  auto range_seg = [&](int item, const Item &it, int b, int u0) {
+    const int st = uniform(sh.start[b]), en = uniform(sh.start[b + 1]);
+    const int blo = max(it.lo, st) - st, bhi = min(it.hi, en) - st;
+    return make_seg(item, it, b, uniform(sh.ctx[b]), blo, bhi, it.share + b,
+                    blo == 0 && bhi == en - st, u0, 0);
+  };
+  // the segment after sg: the next chunk of its range, else the first chunk
+  // of the next non-empty sequence of the share, else the first range of
+  // the next item
+  auto next_seg = [&](const Seg &sg) {
+    Seg nx = sg;
+    nx.valid = 0;
+    if (!sg.valid) return nx;
+    if (!sg.last) {
+      nx.c = sg.c + 1;
+      nx.kn = max(0, min(kIdsUnits, sg.nk - nx.c * kIdsUnits));
+      nx.last = nx.c == max(1, (sg.nk + kIdsUnits - 1) / kIdsUnits) - 1;
+      nx.valid = 1;
+      return nx;
+    }
+    if (!balanced) return nx;
+    const int u0 = sg.u0 + (sg.bhi - sg.blo + NBI - 1) / NBI;
+    int b = sg.b + 1;
+    while (b < B && sh.start[b] < sg.ihi && sh.start[b + 1] == sh.start[b]) ++b;
+    b = uniform(b);
+    if (b < B && uniform(sh.start[b]) < sg.ihi) {
+      const int st = uniform(sh.start[b]), en = uniform(sh.start[b + 1]);
+      const int bhi = min(sg.ihi, en) - st;
+      Seg r = make_seg(sg.item, Item{sg.h0, sg.g, sg.share, 0, sg.ihi}, b, uniform(sh.ctx[b]), 0,
+                       bhi, sg.share + b, bhi == en - st, u0, 0);
+      return r;
+    }
+    if (sg.item != 0 || n_items < 2) return nx;
+    return range_seg(1, items[1], uniform(first_seq_of(sh, B, items[1].lo)), u0);
+  };
+  // lane i: physical id of block i % NBI of the segment's unit i / NBI
+  auto fetch_ids = [&](const Seg &sg) {
+    const int kk = sg.c * kIdsUnits + lane / NBI;
+    const int j = sg.blo + (sg.w0 + kk * NW) * NBI + lane % NBI;
+    const bool ok = sg.valid && kk < sg.nk && j < sg.bhi;
+    const int32_t *row = p.block_tables + (size_t)(sg.valid ? sg.b : 0) * p.max_blocks_per_seq;
+    return row[ok ? j : 0];
+  };
+  // query fragments (A operand) of sequence b: row tl holds head h0 + tl % GH
+  auto load_q = [&](int b, int h0, QOp (&qa)[G::ksteps]) {
     const uint8_t *qrow = p.q + ((size_t)b * Hq + h0 + tl % GH) * D * QB;
     if constexpr (QT == PA_F32) {
       const float *qf = reinterpret_cast<const float *>(qrow);
@@ -335,48 +453,44 @@ __device__ __forceinline__ void run_range(const DecodeParams &p,
       for (int s = 0; s < G::ksteps; ++s)
         qa[s] = *reinterpret_cast<const u32x4 *>(qrow + G::q_elem(s, jq) * QB);
     }
-  }
+  };
 
+  // ---- per-wave softmax state ----------------------------------------------
   float m[4], l[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.0f;
-  }
   float acc[GH][8];
+  auto reset = [&]() {
 #pragma unroll
-  for (int h = 0; h < GH; ++h)
+    for (int v = 0; v < 4; ++v) {
+      m[v] = -INFINITY;
+      l[v] = 0.0f;
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    for (int h = 0; h < GH; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  };
 
   const uint32_t rowstride = (uint32_t)p.num_kv_heads * G::row;
   const uint32_t blk_bytes = rowstride * kBs;          // < 2^31, checked on the host
-  const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;  // head g's row 0 to block end
   const uint32_t k_off = (lane / G::lpk) * rowstride + (lane % G::lpk) * 16;
   uint32_t v_off[G::nvl];
 #pragma unroll
   for (int i = 0; i < G::nvl; ++i) v_off[i] = (i * G::rv + r) * rowstride + c * G::v_piece;
-  const uint8_t *kbase = p.k_cache + (size_t)g * G::row;
-  const uint8_t *vbase = p.v_cache + (size_t)g * G::row;
-  const int32_t *btg = p.block_tables + (size_t)b * p.max_blocks_per_seq;
   const float sl2 = p.scale_log2;
 
-  // Block ids of the wave's units, one chunk of kIdsUnits units at a time:
-  // lane i of `ids` holds the id of block i % NBI of unit k0 + i / NBI, read
-  // with readlane (no memory wait) when that unit's loads are issued.
-  constexpr int kIdsUnits = kWave / NBI;
-  int ids = 0;
-  // Loads of the wave's unit k (chunk starting at k0) into a register stage;
-  // a unit past the end (valid false) loads nothing.
-  auto issue = [&](int k, int k0, bool valid, St &st) {
+  // Loads of one unit of KV head g into a register stage: the unit whose
+  // block ids start at lane u * NBI of `ids`; an invalid unit loads nothing.
+  auto issue = [&](int ids, int u, bool valid, int g, St &st) {
+    // head g's row 0 to the block end
+    const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;
 #pragma unroll
     for (int bi = 0; bi < NBI; ++bi) {
-      const int lidx = min((k - k0) * NBI + bi, kWave - 1);
+      const int lidx = min(u * NBI + bi, kWave - 1);
       const int id = __builtin_amdgcn_readlane(ids, lidx);
-      const size_t off = (size_t)id * blk_bytes;
+      const size_t off = (size_t)id * blk_bytes + (size_t)g * G::row;
       const uint32_t n = valid ? blk_span : 0u;
-      const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase + off, n);
-      const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase + off, n);
+      const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.k_cache + off, n);
+      const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.v_cache + off, n);
 #pragma unroll
       for (int i = 0; i < G::nkl; ++i) st.k[bi][i] = buf_load16(rk, k_off + i * G::rvk * rowstride);
 #pragma unroll
@@ -384,8 +498,7 @@ __device__ __forceinline__ void run_range(const DecodeParams &p,
     }
   };
 
-  auto compute_unit = [&](int k, const St &st) {
-    const int jb = blo + (wave + k * kWaves) * NBI;
+  auto compute_unit = [&](int jb, int tok_lim, const QOp (&qa)[G::ksteps], const St &st) {
     // logits, log2 domain; masked tokens -inf
     float sv[NBI][4];
     // K tile: registers (row-contiguous) -> LDS -> MFMA operand layout, in
@@ -475,172 +588,232 @@ __device__ __forceinline__ void run_range(const DecodeParams &p,
     wave_lds_fence();
   };
 
-  // The wave's units k = 0 .. nk-1 (unit wave + k * kWaves of the range)
-  // through NS register stages in turn: while unit k is computed, the loads
-  // of units k+1 .. k+NS-1 are in flight. Every load instruction is issued
-  // unconditionally (past the end they read nothing), so the compiler's
-  // memory-counter waits stay exact: computing unit k waits only for unit k.
-  const int nk = wave < nunits ? (nunits - wave + kWaves - 1) / kWaves : 0;
-  for (int k0 = 0; k0 < nk; k0 += kIdsUnits) {
-    const int kn = min(nk - k0, kIdsUnits);
-    {
-      const int kk = k0 + lane / NBI;
-      const int j = blo + (wave + kk * kWaves) * NBI + lane % NBI;
-      ids = btg[(kk < nk && j < bhi) ? j : blo];
+  // end of a range: merge the waves' softmax states and write the range's
+  // partial (or the output, for a whole sequence)
+  auto epilogue = [&](int b, int piece, bool whole, int h0) {
+    // merge the waves: sums over the token lanes / rows, then across waves
+  #pragma unroll
+    for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
+    if (4 * jq < GH && tl == 0) {
+  #pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (v < GH) {
+          sh.m[wave][4 * jq + v] = m[v];
+          sh.l[wave][4 * jq + v] = l[v];
+        }
     }
-    St st[NS];
+  #pragma unroll
+    for (int h = 0; h < GH; ++h)
+  #pragma unroll
+      for (int e = 0; e < 8; ++e)
+  #pragma unroll
+        for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
+    if (r == 0) {
+  #pragma unroll
+      for (int h = 0; h < GH; ++h)
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) sh.acc[wave][h][c * 8 + e] = acc[h][e];
+    }
+    __syncthreads();
+
+    const bool to_out = whole && p.direct;
+    for (int i = tid; i < GH * D; i += (NW * kWave)) {
+      const int h = i / D, d = i % D;
+      float M = -INFINITY;
+  #pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sh.m[w][h]);
+      float L = 0.0f, O = 0.0f;
+  #pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(sh.m[w][h] - M);
+        L += sh.l[w][h] * sc;
+        O += sh.acc[w][h][d] * sc;
+      }
+      const float res = O * p.v_scale / L;
+      const size_t bh = (size_t)b * Hq + h0 + h;
+      if (to_out) {
+        store_elem<QT>(p.out, bh * D + d, res);
+      } else {
+        const size_t pi = (p.mode == kSplitBalanced)
+                              ? (size_t)(h0 + h) * p.max_partitions + piece
+                              : bh * p.max_partitions + piece;
+        p.tmp_out[pi * D + d] = res;
+        if (d == 0) {
+          p.max_logits[pi] = M * kLn2;
+          p.exp_sums[pi] = L;
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- the stream ------------------------------------------------------------
+  Seg cur = make_seg(0, items[0], b_first, n_first, blo_first, bhi_first, piece_first,
+                     whole_first, 0, 0);
+  Seg nxt = next_seg(cur);
+  int ids_cur = fetch_ids(cur);
+  QOp q_cur[G::ksteps], q_nxt[G::ksteps];
+  load_q(cur.b, items[0].h0, q_cur);
+  St st[NS];
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(k0 + s, k0, s < kn, st[s]);
-    for (int k = 0; k < kn; k += NS) {
+  for (int s = 0; s < NS - 1; ++s) issue(ids_cur, s, s < cur.kn, cur.g, st[s]);
+  int ids_nxt = fetch_ids(nxt);
+  load_q(nxt.valid ? nxt.b : cur.b, nxt.valid ? nxt.h0 : cur.h0, q_nxt);
+  reset();
+  for (;;) {
+    // Units k = 0 .. kn-1 of the segment through NS register stages in turn:
+    // while unit k is computed, the loads of units k+1 .. k+NS-1 are in
+    // flight; indices from kpad on are the next segment's first units, which
+    // land in the stages its own loop starts from. Every load instruction is
+    // issued unconditionally (past the end they read nothing), so the
+    // compiler's memory-counter waits stay exact: computing a unit waits only
+    // for that unit.
+    const int kn = cur.kn;
+    const int kpad = max(NS, (kn + NS - 1) / NS * NS);
+    const int g_cur = cur.g, g_nxt = nxt.valid ? nxt.g : cur.g;
+    const int jb0 = cur.blo + (cur.w0 + cur.c * kIdsUnits * NW) * NBI;
+    const int tok_lim = min(cur.bhi * kBs, cur.n);
+    for (int k = 0; k < kpad - NS; k += NS) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        issue(k0 + k + s + NS - 1, k0, k + s + NS - 1 < kn, st[(s + NS - 1) % NS]);
-        if (k + s < kn) compute_unit(k0 + k + s, st[s]);
+        const int u = k + s + NS - 1;
+        issue(ids_cur, u, u < kn, g_cur, st[(s + NS - 1) % NS]);
+        if (k + s < kn) compute_unit(jb0 + (k + s) * NW * NBI, tok_lim, q_cur, st[s]);
       }
     }
-  }
-
-  // merge the waves: sums over the token lanes / rows, then across waves
+    // the last step, peeled: it issues this segment's last unit and the
+    // next segment's first NS - 1 units (so that the ids of the next
+    // segment are read only here, where their load is long done)
+    {
+      const int k = kpad - NS;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
-  if (4 * jq < GH && tl == 0) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (v < GH) {
-        sh.m[wave][4 * jq + v] = m[v];
-        sh.l[wave][4 * jq + v] = l[v];
-      }
-  }
-#pragma unroll
-  for (int h = 0; h < GH; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
-  if (r == 0) {
-#pragma unroll
-    for (int h = 0; h < GH; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sh.acc[wave][h][c * 8 + e] = acc[h][e];
-  }
-  __syncthreads();
-
-  const bool to_out = whole && p.direct;
-  for (int i = tid; i < GH * D; i += kThreads) {
-    const int h = i / D, d = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.m[w][h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = __builtin_amdgcn_exp2f(sh.m[w][h] - M);
-      L += sh.l[w][h] * sc;
-      O += sh.acc[w][h][d] * sc;
-    }
-    const float res = O * p.v_scale / L;
-    const size_t bh = (size_t)b * Hq + h0 + h;
-    if (to_out) {
-      store_elem<QT>(p.out, bh * D + d, res);
-    } else {
-      const size_t pi = (p.mode == kSplitBalanced)
-                            ? (size_t)(h0 + h) * p.max_partitions + piece
-                            : bh * p.max_partitions + piece;
-      p.tmp_out[pi * D + d] = res;
-      if (d == 0) {
-        p.max_logits[pi] = M * kLn2;
-        p.exp_sums[pi] = L;
+      for (int s = 0; s < NS; ++s) {
+        if (s == 0) issue(ids_cur, kpad - 1, kpad - 1 < kn, g_cur, st[NS - 1]);
+        else issue(ids_nxt, s - 1, nxt.valid && s - 1 < nxt.kn, g_nxt, st[s - 1]);
+        if (k + s < kn) compute_unit(jb0 + (k + s) * NW * NBI, tok_lim, q_cur, st[s]);
       }
     }
+    // move to the next segment (copies of loads issued a segment ago, made
+    // before the epilogue's stores so that their waits do not cover the
+    // next segment's loads already in flight)
+    const Seg done = cur;
+    cur = nxt;
+    ids_cur = ids_nxt;
+#pragma unroll
+    for (int s = 0; s < G::ksteps; ++s) q_cur[s] = q_nxt[s];
+    if (done.last) {
+      epilogue(done.b, done.piece, done.whole, done.h0);
+      reset();
+    }
+    if (!cur.valid) break;
+    nxt = next_seg(cur);
+    ids_nxt = fetch_ids(nxt);
+    load_q(nxt.valid ? nxt.b : cur.b, nxt.valid ? nxt.h0 : cur.h0, q_nxt);
   }
-  __syncthreads();
 }
 
 __device__ __forceinline__ int num_blocks_of(int n) { return n > 0 ? (n + kBs - 1) / kBs : 0; }
 
-template <int QT, int KT, int D, int GH, int NBI, int NS>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
-  __shared__ Shared<QT, KT, D, GH, NBI> sh;
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
+  __shared__ Shared<QT, KT, D, GH, NBI, NW> sh;
   const int tid = threadIdx.x;
-  const int h0 = blockIdx.y * GH;  // first query head of this workgroup
-  const int g = h0 / p.group;      // its KV head
 
+  Item items[2];
+  int n_items = 1;
+  // the first range: blocks [first_lo, first_hi) of sequence first_b
+  int first_b = 0, first_n = 0, first_lo = 0, first_hi = 0, first_piece = 0;
+  bool first_whole = false;
   if (p.mode != kSplitBalanced) {
+    const int h0 = blockIdx.y * GH;  // first query head of this workgroup
     const int b = blockIdx.z;
     const int part = blockIdx.x;
     const int n = p.context_lens[b];
     if (n <= 0) {
       if (p.mode == kSplitSingle)
-        for (int i = tid; i < GH * D; i += kThreads)
+        for (int i = tid; i < GH * D; i += (NW * kWave))
           store_elem<QT>(p.out, ((size_t)b * p.num_q_heads + h0) * D + i, 0.0f);
       return;
     }
     const int nblk = num_blocks_of(n);
     const int blo = part * p.partition_blocks;
     if (blo >= nblk) return;
-    const int bhi = min(nblk, blo + p.partition_blocks);
-    run_range<QT, KT, D, GH, NBI, NS>(p, sh, b, blo, bhi, part, nblk <= p.partition_blocks, h0, g);
-    return;
-  }
-
-  // Balanced split: the blocks of all sequences, end to end, cut into
-  // num_splits equal shares; share s = blockIdx.x. First the start block of
-  // every sequence (exclusive prefix sum of ceil(n / 16)).
-  const int B = p.num_seqs;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
-  {
-    constexpr int PER = kMaxBalancedSeqs / kThreads;
-    int cnt[PER];
-    int tot = 0;
+    items[0] = Item{h0, h0 / p.group, 0, 0, 0};
+    first_b = b;
+    first_n = n;
+    first_lo = blo;
+    first_hi = min(nblk, blo + p.partition_blocks);
+    first_piece = part;
+    first_whole = nblk <= p.partition_blocks;
+  } else {
+    // Balanced split: the blocks of all sequences, end to end, cut into
+    // num_splits equal shares. First the start block of every sequence
+    // (exclusive prefix sum of ceil(n / 16)).
+    const int B = p.num_seqs;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    {
+      constexpr int PER = kMaxBalancedSeqs / (NW * kWave);
+      int cnt[PER];
+      int tot = 0;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int bb = PER * tid + k;
-      cnt[k] = bb < B ? num_blocks_of(p.context_lens[bb]) : 0;
-      tot += cnt[k];
-    }
-    int incl = tot;
+      for (int k = 0; k < PER; ++k) {
+        const int bb = PER * tid + k;
+        const int n = bb < B ? p.context_lens[bb] : 0;
+        if (bb < B) sh.ctx[bb] = n;
+        cnt[k] = num_blocks_of(n);
+        tot += cnt[k];
+      }
+      int incl = tot;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (lane == kWave - 1) sh.wave_sum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += sh.wave_sum[w];
-    int ex = base + incl - tot;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      if (lane == kWave - 1) sh.wave_sum[wave] = incl;
+      __syncthreads();
+      int base = 0;
+      for (int w = 0; w < wave; ++w) base += sh.wave_sum[w];
+      int ex = base + incl - tot;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int bb = PER * tid + k;
-      if (bb < B) sh.start[bb] = ex;
-      ex += cnt[k];
+      for (int k = 0; k < PER; ++k) {
+        const int bb = PER * tid + k;
+        if (bb < B) sh.start[bb] = ex;
+        ex += cnt[k];
+      }
+      if (tid == (NW * kWave) - 1) sh.start[B] = base + incl;
+      __syncthreads();
     }
-    if (tid == kThreads - 1) sh.start[B] = base + incl;
-    __syncthreads();
+    const int total = uniform(sh.start[B]);
+    // at most one share per block, so that no share is empty
+    const int S = min(p.num_splits, total);
+    // Workgroup (x, y) takes share 2x of its own head row y and share 2x + 1
+    // of the paired row y ^ 1 (the pair's other workgroup takes the other
+    // two). The cache rows of neighbouring KV heads sit in different halves
+    // of the memory interleave, which the hardware serves at different
+    // rates; pairing gives every workgroup the same mix.
+    const int y = blockIdx.y;
+    const int y2 = (y ^ 1) < (int)gridDim.y ? (y ^ 1) : y;
+    const int s0 = 2 * blockIdx.x;
+    if (s0 >= S) return;
+    n_items = s0 + 1 < S ? 2 : 1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int s = min(s0 + k, S - 1);
+      const int h0 = (k == 0 ? y : y2) * GH;
+      items[k] = Item{h0, h0 / p.group, s, (int)((long long)s * total / S),
+                      (int)((long long)(s + 1) * total / S)};
+    }
+    first_b = uniform(first_seq_of(sh, B, items[0].lo));
+    const int st = uniform(sh.start[first_b]), en = uniform(sh.start[first_b + 1]);
+    first_n = uniform(sh.ctx[first_b]);
+    first_lo = items[0].lo - st;
+    first_hi = min(items[0].hi, en) - st;
+    first_piece = items[0].share + first_b;
+    first_whole = first_lo == 0 && first_hi == en - st;
   }
-  const int total = sh.start[B];
-  // at most one share per block, so that no share is empty
-  const int S = min(p.num_splits, total);
-  const int s = blockIdx.x;
-  if (s >= S) return;
-  const int lo = (int)((long long)s * total / S);
-  const int hi = (int)((long long)(s + 1) * total / S);
-  if (lo >= hi) return;
-  // the sequence holding block lo: the largest b with start[b] <= lo
-  int bl = 0, bh = B - 1;
-  while (bl < bh) {
-    const int mid = (bl + bh + 1) >> 1;
-    if (sh.start[mid] <= lo) bl = mid;
-    else bh = mid - 1;
-  }
-  for (int b = bl; b < B; ++b) {
-    const int st = sh.start[b], en = sh.start[b + 1];
-    if (st >= hi) break;
-    if (en <= lo || en == st) continue;
-    const int blo = max(lo, st) - st, bhi = min(hi, en) - st;
-    run_range<QT, KT, D, GH, NBI, NS>(p, sh, b, blo, bhi, s + b, blo == 0 && bhi == en - st, h0, g);
-  }
+  run_ranges<QT, KT, D, GH, NBI, NS, NW>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
+                                     first_piece, first_whole);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,40 +951,63 @@ constexpr int units_of() {
 }
 
 
+// Waves of a balanced-split workgroup: eight (one workgroup per compute
+// unit: the hardware serves the workgroups of a compute unit unevenly, the
+// waves of one workgroup alike) where two waves per SIMD fit the registers
+// without spills, else four.
 template <int QT, int KT, int D, int GH>
-const void *kernel_of() {
-  return reinterpret_cast<const void *>(
-      &decode_kernel<QT, KT, D, GH, units_of<QT, KT, GH>(), kStages>);
+constexpr int balanced_waves() {
+  if (GH > 8) return 4;
+  if (QT == PA_F32) return (D == 64 || GH == 1) ? 8 : 4;
+  return 8;
+}
+
+struct KernelRef {
+  const void *fn;
+  int threads;
+};
+
+template <int QT, int KT, int D, int GH>
+KernelRef kernel_of(bool balanced) {
+  constexpr int NBI = units_of<QT, KT, GH>();
+  constexpr int NWB = balanced_waves<QT, KT, D, GH>();
+  if (balanced)
+    return {reinterpret_cast<const void *>(&decode_kernel<QT, KT, D, GH, NBI, kStages, NWB>),
+            NWB * kWave};
+  return {reinterpret_cast<const void *>(&decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves>),
+          kFixedWaves * kWave};
 }
 
 template <int QT, int KT, int D>
-const void *by_gh(int gh) {
+KernelRef by_gh(int gh, bool balanced) {
   switch (gh) {
-    case 1: return kernel_of<QT, KT, D, 1>();
-    case 2: return kernel_of<QT, KT, D, 2>();
-    case 4: return kernel_of<QT, KT, D, 4>();
-    case 8: return kernel_of<QT, KT, D, 8>();
-    case 16: return kernel_of<QT, KT, D, 16>();
+    case 1: return kernel_of<QT, KT, D, 1>(balanced);
+    case 2: return kernel_of<QT, KT, D, 2>(balanced);
+    case 4: return kernel_of<QT, KT, D, 4>(balanced);
+    case 8: return kernel_of<QT, KT, D, 8>(balanced);
+    case 16: return kernel_of<QT, KT, D, 16>(balanced);
   }
-  return nullptr;
+  return {nullptr, 0};
 }
 
 template <int QT, int KT>
-const void *by_d(int d, int gh) {
+KernelRef by_d(int d, int gh, bool balanced) {
   switch (d) {
-    case 64: return by_gh<QT, KT, 64>(gh);
-    case 128: return by_gh<QT, KT, 128>(gh);
+    case 64: return by_gh<QT, KT, 64>(gh, balanced);
+    case 128: return by_gh<QT, KT, 128>(gh, balanced);
   }
-  return nullptr;
+  return {nullptr, 0};
 }
 
-const void *decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh) {
-  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return by_d<PA_F32, PA_F32>(d, gh);
-  if (q_dtype == PA_F16 && kv_dtype == PA_F16) return by_d<PA_F16, PA_F16>(d, gh);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return by_d<PA_BF16, PA_BF16>(d, gh);
-  if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN) return by_d<PA_F16, PA_FP8_E4M3FN>(d, gh);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN) return by_d<PA_BF16, PA_FP8_E4M3FN>(d, gh);
-  return nullptr;
+KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, bool balanced) {
+  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return by_d<PA_F32, PA_F32>(d, gh, balanced);
+  if (q_dtype == PA_F16 && kv_dtype == PA_F16) return by_d<PA_F16, PA_F16>(d, gh, balanced);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return by_d<PA_BF16, PA_BF16>(d, gh, balanced);
+  if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN)
+    return by_d<PA_F16, PA_FP8_E4M3FN>(d, gh, balanced);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN)
+    return by_d<PA_BF16, PA_FP8_E4M3FN>(d, gh, balanced);
+  return {nullptr, 0};
 }
 
 }  // namespace
@@ -819,7 +1015,7 @@ const void *decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh) {
 // Workgroups of one decode kernel that fill a device once: compute units x
 // resident workgroups per unit. Looked up once per (device, kernel) and kept
 // for the life of the process (a device property, not state of a call).
-int fill_workgroups(const void *fn) {
+int fill_workgroups(const void *fn, int threads) {
   static std::mutex mu;
   static std::map<std::pair<int, const void *>, int> cache;
   int dev = 0;
@@ -833,7 +1029,7 @@ int fill_workgroups(const void *fn) {
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -844,12 +1040,13 @@ int fill_workgroups(const void *fn) {
 
 int balanced_num_splits(const DecodeLaunch &a) {
   const int gh = heads_per_workgroup(a.num_q_heads / a.num_kv_heads);
-  const void *fn = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh);
-  if (!fn) return 2;
-  const int cus = fill_workgroups(fn);
+  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, true);
+  if (!k.fn) return 2;
+  const int cus = fill_workgroups(k.fn, k.threads);
   if (cus <= 0) return kMaxAutoSplits / 8;
   const long long groups = (long long)a.num_kv_heads * (a.num_q_heads / a.num_kv_heads / gh);
-  long long s = ((long long)cus + groups - 1) / groups;
+  // two shares per workgroup, as many workgroups as fit at once
+  long long s = 2 * (((long long)cus + groups - 1) / groups);
   if (s < 2) s = 2;
   if (s > kMaxAutoSplits) s = kMaxAutoSplits;
   return (int)s;
@@ -881,15 +1078,16 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.scale_log2 = a.scale * ks * kLog2e;
   p.v_scale = a.kv_dtype == PA_FP8_E4M3FN ? a.v_scale : 1.0f;
   const int gh = heads_per_workgroup(p.group);
-  const void *fn = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh);
-  if (!fn) return (int)hipErrorInvalidValue;
+  const KernelRef k =
+      decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, a.mode == kSplitBalanced);
+  if (!k.fn) return (int)hipErrorInvalidValue;
   const int head_groups = a.num_kv_heads * (p.group / gh);
   dim3 grid;
-  if (a.mode == kSplitBalanced) grid = dim3(a.num_splits, head_groups, 1);
+  if (a.mode == kSplitBalanced) grid = dim3((a.num_splits + 1) / 2, head_groups, 1);
   else if (a.mode == kSplitFixed) grid = dim3(a.max_partitions, head_groups, a.num_seqs);
   else grid = dim3(1, head_groups, a.num_seqs);
   void *args[] = {&p};
-  hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), args, 0,
+  hipError_t e = hipLaunchKernel(k.fn, grid, dim3(k.threads), args, 0,
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return (int)e;
   return (int)hipGetLastError();
