@@ -285,6 +285,7 @@ struct Shared {
   int start[kMaxBalancedSeqs + 1];  // balanced split: first block of each sequence
   int ctx[kMaxBalancedSeqs];        // balanced split: context length of each sequence
   int wave_sum[NW];
+  int first[2];  // balanced split: the sequence holding the first block of each share taken
 };
 
 template <int QT, int KT, int D, int GH, int NBI>
@@ -323,19 +324,6 @@ struct Seg {
   int last;   // last segment of its range: the range's epilogue follows it
   int valid;
 };
-
-// The sequence holding block x of the blocks end to end (the largest b with
-// start[b] <= x; it holds blocks since start[b + 1] > x).
-template <class Sh>
-__device__ __forceinline__ int first_seq_of(const Sh &sh, int B, int x) {
-  int bl = 0, bh = B - 1;
-  while (bl < bh) {
-    const int mid = (bl + bh + 1) >> 1;
-    if (sh.start[mid] <= x) bl = mid;
-    else bh = mid - 1;
-  }
-  return bl;
-}
 
 // All ranges of a workgroup's work items (one range, or the ranges of one
 // or two balanced shares), all waves. The segments of a wave form one
@@ -425,7 +413,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       return r;
     }
     if (sg.item != 0 || n_items < 2) return nx;
-    return range_seg(1, items[1], uniform(first_seq_of(sh, B, items[1].lo)), u0);
+    return range_seg(1, items[1], uniform(sh.first[1]), u0);
   };
   // lane i: physical id of block i % NBI of the segment's unit i / NBI
   auto fetch_ids = [&](const Seg &sg) {
@@ -650,10 +638,11 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   // ---- the stream ------------------------------------------------------------
   Seg cur = make_seg(0, items[0], b_first, n_first, blo_first, bhi_first, piece_first,
                      whole_first, 0, 0);
-  Seg nxt = next_seg(cur);
+  // the first segment's loads go out before the LDS walk to the next one
   int ids_cur = fetch_ids(cur);
   QOp q_cur[G::ksteps], q_nxt[G::ksteps];
   load_q(cur.b, items[0].h0, q_cur);
+  Seg nxt = next_seg(cur);
   St st[NS];
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(ids_cur, s, s < cur.kn, cur.g, st[s]);
@@ -772,13 +761,25 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       }
       if (lane == kWave - 1) sh.wave_sum[wave] = incl;
       __syncthreads();
-      int base = 0;
-      for (int w = 0; w < wave; ++w) base += sh.wave_sum[w];
+      int base = 0, all = 0;
+      for (int w = 0; w < NW; ++w) {
+        const int ws = sh.wave_sum[w];
+        if (w < wave) base += ws;
+        all += ws;
+      }
+      // the first blocks of this workgroup's shares (see below), and the
+      // sequences holding them: each thread checks its own sequences
+      const int S = min(p.num_splits, all);
+      const int s0 = 2 * blockIdx.x;
+      const long long f0 = s0 < S ? (long long)s0 * all / S : -1;
+      const long long f1 = s0 + 1 < S ? (long long)(s0 + 1) * all / S : -1;
       int ex = base + incl - tot;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int bb = PER * tid + k;
         if (bb < B) sh.start[bb] = ex;
+        if (ex <= f0 && f0 < ex + cnt[k]) sh.first[0] = bb;
+        if (ex <= f1 && f1 < ex + cnt[k]) sh.first[1] = bb;
         ex += cnt[k];
       }
       if (tid == (NW * kWave) - 1) sh.start[B] = base + incl;
@@ -804,7 +805,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       items[k] = Item{h0, h0 / p.group, s, (int)((long long)s * total / S),
                       (int)((long long)(s + 1) * total / S)};
     }
-    first_b = uniform(first_seq_of(sh, B, items[0].lo));
+    first_b = uniform(sh.first[0]);
     const int st = uniform(sh.start[first_b]), en = uniform(sh.start[first_b + 1]);
     first_n = uniform(sh.ctx[first_b]);
     first_lo = items[0].lo - st;
