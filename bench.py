@@ -41,7 +41,9 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
 DEFAULT_WORKLOAD = "llama3_8b_b32"
 DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn"}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1}
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_426_amd", "csrc", "pa_decode.hip")
+# the decode kernel's sources (the traffic counters are tied to them)
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_426_amd", "csrc", f)
+               for f in ("pa_decode_kernel.h", "pa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3_8b_b32_traffic.md")
 
 
@@ -57,6 +59,9 @@ def parse_args(argv=None):
     ap.add_argument("--layers", type=int, default=4,
                     help="layer caches rotated over (defeats the last-level cache)")
     ap.add_argument("--roofline-launches", type=int, default=400)
+    ap.add_argument("--fused-append", action="store_true",
+                    help="one decode-with-append launch instead of the slot-write kernel "
+                         "followed by decode (measured no faster on these workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -111,6 +116,32 @@ def write_bytes(wl):
     return n * 2 * row * (ELEM_BYTES[wl.q_dtype] + ELEM_BYTES[wl.kv_dtype]) + 8 * len(wl.new_slots)
 
 
+def append_bytes(wl):
+    """Decode with append, beyond the decode's own bytes: each new token's K/V
+    rows are read from the inputs and written to the slot, and its cache rows,
+    which the decode's count includes, need not be read."""
+    if wl.new_slots is None:
+        return 0
+    n = int((wl.new_slots >= 0).sum())
+    row = wl.num_kv_heads * wl.head_dim
+    return n * 2 * row * ELEM_BYTES[wl.q_dtype]
+
+
+def new_token_is_last(wl):
+    """Every sequence's new token sits at its last position (what decode with
+    append assumes)."""
+    import numpy as np
+
+    if wl.new_slots is None:
+        return False
+    bs = wl.block_size
+    for b, n in enumerate(wl.context_lens):
+        want = -1 if n <= 0 else int(wl.block_tables[b, (n - 1) // bs]) * bs + (n - 1) % bs
+        if int(wl.new_slots[b]) != want:
+            return False
+    return True
+
+
 def copy_bytes(wl):
     blk = wl.block_size * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
     return len(wl.cow_pairs) * 2 * 2 * blk
@@ -121,8 +152,11 @@ def copy_bytes(wl):
 # ---------------------------------------------------------------------------
 
 def decode_source_hash():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(workload, partition_size):
@@ -247,10 +281,20 @@ def main(argv=None):
     has_cow = len(wl.cow_pairs) > 0
     torch.cuda.synchronize()
 
+    # With --fused-append the slot write rides in the decode launch
+    # (decode_append), which needs every new token at its sequence's last
+    # position.
+    fused = new_s is not None and args.fused_append and new_token_is_last(wl)
+
     def step(i):
         kc, vc = layers[i % len(layers)]
         if has_cow:
             pa.copy_blocks(kc, vc, cow)
+        if fused:
+            pa.decode_append(q, new_k, new_v, kc, vc, bt, cl, scale=wl.scale,
+                             k_scale=wl.k_scale, v_scale=wl.v_scale, partition_size=P,
+                             out=out, workspace=ws)
+            return
         if new_s is not None:
             pa.reshape_and_cache(new_k, new_v, kc, vc, new_s, wl.k_scale, wl.v_scale)
         pa.decode(q, kc, vc, bt, cl, scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
@@ -339,7 +383,7 @@ def main(argv=None):
     kernel_alg = db["kv"] + db["q"] + db["tables"] + db["ctx_lens"]
     if not P:
         kernel_alg += db["out"]
-    step_alg = db["total"] + write_bytes(wl) + copy_bytes(wl)
+    step_alg = db["total"] + (append_bytes(wl) if fused else write_bytes(wl)) + copy_bytes(wl)
     tokens = wl.tokens_attended
     step_s = ms_per_step / 1e3
     achieved = kernel_alg / kern_avg_s / 1e9
@@ -373,7 +417,8 @@ def main(argv=None):
             "partition_size": P,
             "layers_rotated": args.layers,
             "step": ("copy_blocks + " if has_cow else "") +
-                    "reshape_and_cache(new tokens) + decode" +
+                    ("decode_append (new tokens' slot writes in the decode launch)" if fused
+                     else "reshape_and_cache(new tokens) + decode") +
                     (" (partials + merge)" if P else " (single pass)"),
         },
         "gbps": step_alg / step_s / 1e9,
@@ -386,7 +431,8 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": committed_traffic(wl.name, P),
-            "kernel": "decode_kernel" + (" (split partials)" if P else " (single pass)"),
+            "kernel": "decode_kernel" + (" (split partials)" if P else " (single pass)") +
+                      ("; the step runs its variant with the slot write fused" if fused else ""),
             "kernel_avg_us": kern_avg_s * 1e6,
             "kernel_median_us": kern_med_s * 1e6,
             "algorithmic_bytes_per_launch": kernel_alg,

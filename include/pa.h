@@ -176,6 +176,43 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     void *stream);
 
 /*
+ * pa_decode_append -- one decode step with the new token appended.
+ *
+ * The decode phase ("vLLM inference principles", two phases: decode) extends
+ * each sequence's cache by the new token's K/V and then lets its query attend
+ * over the whole context, the new token included. Here the new token of
+ * sequence b is its last position, n - 1 with n = context_lens[b] > 0:
+ *
+ *   1. key[b], value[b] are written to slot
+ *        block_tables[b][(n - 1) / block_size] * block_size + (n - 1) % block_size
+ *      of k_cache / v_cache, exactly as pa_reshape_and_cache writes them
+ *      (a bit copy, or fp8 e4m3fn of x / k_scale resp. x / v_scale);
+ *   2. out = pa_decode(...) over the caches after that write.
+ *
+ * Both happen in one kernel launch (plus the merge of a split): the
+ * workgroups that attend over a sequence's last block take the new token's
+ * rows from key / value and one of them writes them to the cache. The result
+ * (caches and out) equals pa_reshape_and_cache with those slots followed by
+ * pa_decode, bit for bit.
+ *
+ * Arguments as pa_decode, plus:
+ *   key, value    [num_seqs, num_kv_heads, head_dim], device, in q_dtype. Rows
+ *                 of sequences with n = 0 are not read.
+ *   k_cache, v_cache  written at the new tokens' slots only.
+ * The block holding position n - 1 must be private to sequence b (copy a
+ * shared block with pa_copy_blocks first). fp8 caches need finite, non-zero
+ * k_scale and v_scale (PA_ERR_BAD_SHAPE otherwise); NULL key or value gives
+ * PA_ERR_NULL_POINTER. Other errors as pa_decode.
+ */
+pa_status pa_decode_append(void *out, const void *q, const void *key, const void *value,
+                           void *k_cache, void *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, float scale, int q_dtype, int kv_dtype,
+                           float k_scale, float v_scale, int partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * pa_decode_partials -- the per-piece half of split-context decode.
  *
  * For each piece (a fixed partition p of sequence b, or a balanced-split

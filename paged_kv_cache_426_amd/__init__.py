@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_workspace_size.argtypes = [i32] * 6
         L.pa_decode.restype = i32
         L.pa_decode.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, f32, f32, i32, vp, sz, vp]
+        L.pa_decode_append.restype = i32
+        L.pa_decode_append.argtypes = ([vp] * 8 + [i32] * 7 +
+                                       [f32, i32, i32, f32, f32, i32, vp, sz, vp])
         L.pa_decode_partials.restype = i32
         L.pa_decode_partials.argtypes = ([vp] * 3 + [i32] + [vp] * 5 + [i32] * 7 +
                                          [f32, i32, i32, f32, f32, i32, vp])
@@ -185,6 +188,39 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            _ptr(context_lens), B, Hq, Hkv, d, bs, NB, MBS, float(scale),
                            dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
                            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def decode_append(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: Optional[float] = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                  out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step with the new token appended (C: pa_decode_append): key
+    and value [B, Hkv, d] (q's type) are written to each sequence's last
+    position, then out = decode over the caches. Returns out [B, Hq, d]."""
+    dev = _dev(q, key, value, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if key.shape != (B, Hkv, d) or value.shape != key.shape or key.dtype != q.dtype or \
+            value.dtype != q.dtype:
+        raise PaError("key and value must be [B, Hkv, d] in q's type")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PaError("out must match q in shape and type")
+    need = decode_workspace_size(B, Hq, d, MBS, bs, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_append(_ptr(out), _ptr(q), _ptr(key.contiguous()),
+                                  _ptr(value.contiguous()), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs, NB,
+                                  MBS, float(scale), dtype_code(q), dtype_code(k_cache),
+                                  float(k_scale), float(v_scale), int(partition_size),
+                                  _ptr(workspace), ws_bytes, _stream(dev)))
     return out
 
 

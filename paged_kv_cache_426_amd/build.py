@@ -2,10 +2,13 @@
 
     python -m paged_kv_cache_426_amd.build [--verbose]
 
-Every call compiles from source (no caching), writing
+Every call compiles from source (no caching): each source file to an object
+in its own hipcc process, in parallel (the decode kernels are split one
+element-type pair per file for this), then links
 ``paged_kv_cache_426_amd/libpa.so`` atomically.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -18,7 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_cache.hip"]
+SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_cache.hip", "pa_decode_f32_f32.hip",
+           "pa_decode_f16_f16.hip", "pa_decode_bf16_bf16.hip", "pa_decode_f16_fp8.hip",
+           "pa_decode_bf16_fp8.hip"]
 
 ARCH = "gfx950"
 
@@ -27,7 +32,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 instructions are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # the fp8 slot write divides by the scale: IEEE float32 division
@@ -45,23 +49,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libpa.so cannot be built")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix=".libpa.", suffix=".so.tmp", dir=PKG)
-    os.close(fd)
-    cmd = [hipcc(), *FLAGS, *extra_flags, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _compile(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; that is harmless
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
-    if res.returncode != 0:
-        os.unlink(tmp)
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    cc = hipcc()
+    objdir = tempfile.mkdtemp(prefix=".libpa_obj.", dir=PKG)
+    try:
+        cmds = []
+        objs = []
+        for name in SOURCES:
+            obj = os.path.join(objdir, name + ".o")
+            objs.append(obj)
+            cmds.append([cc, *FLAGS, *extra_flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+                         os.path.join(CSRC, name), "-o", obj])
+        fd, tmp = tempfile.mkstemp(prefix=".libpa.", suffix=".so.tmp", dir=PKG)
+        os.close(fd)
+        cmds.append([cc, *FLAGS, *extra_flags, "-shared", *objs, "-o", tmp])
+        workers = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 16))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            results = list(pool.map(_compile, cmds[:-1]))
+        results.append(_compile(cmds[-1]) if all(r == 0 for r, _ in results)
+                       else (1, ["(not linked: a compile step failed)"]))
+        failed = []
+        for cmd, (rc, msgs) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+                if msgs:
+                    print("\n".join(msgs))
+            if rc != 0:
+                failed.append(" ".join(cmd) + "\n" + "\n".join(msgs))
+        if failed:
+            os.unlink(tmp)
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB
 
 

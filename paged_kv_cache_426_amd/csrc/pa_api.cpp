@@ -196,12 +196,16 @@ pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_log
   return status_of(pa::launch_reduce(r, stream));
 }
 
-pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                    const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
-                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                    int num_blocks, int max_blocks_per_seq, float scale, int q_dtype,
-                    int kv_dtype, float k_scale, float v_scale, int partition_size,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// pa_decode, and pa_decode_append when new_k / new_v are given.
+pa_status decode_impl(void *out, const void *q, const void *new_k, const void *new_v,
+                      const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      int max_blocks_per_seq, float scale, int q_dtype, int kv_dtype,
+                      float k_scale, float v_scale, int partition_size, void *workspace,
+                      size_t workspace_bytes, void *stream) {
   if (!out) return PA_ERR_NULL_POINTER;
   pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -210,6 +214,8 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
   if (st != PA_OK) return st;
   pa::DecodeLaunch a{};
   a.out = out;
+  a.new_k = new_k;
+  a.new_v = new_v;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -279,6 +285,38 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
   r.skip_single = 1;
   r.out_dtype = q_dtype;
   return status_of(pa::launch_reduce(r, stream));
+}
+
+}  // namespace
+
+pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, int max_blocks_per_seq, float scale, int q_dtype,
+                    int kv_dtype, float k_scale, float v_scale, int partition_size,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(void *out, const void *q, const void *key, const void *value,
+                           void *k_cache, void *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, float scale, int q_dtype, int kv_dtype,
+                           float k_scale, float v_scale, int partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  if (!key || !value) return PA_ERR_NULL_POINTER;
+  // the new token's rows are written as pa_reshape_and_cache writes them
+  if (kv_dtype == PA_FP8_E4M3FN &&
+      (!isfinite(k_scale) || !isfinite(v_scale) || k_scale == 0.0f || v_scale == 0.0f))
+    return PA_ERR_BAD_SHAPE;
+  return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache, void *v_cache,

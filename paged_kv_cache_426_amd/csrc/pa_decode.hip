@@ -1,821 +1,16 @@
-// Paged-attention decode for gfx950 (CDNA4, wave64).
-//
-// What is computed: for each sequence b and query head h, one query row
-// attends over the sequence's n cached tokens, softmax(q K^T * scale) V
-// ("KV-Cache evolution" §1, attention formula), where token j's K/V row sits
-// in physical block block_tables[b][j / 16] at offset j % 16 ("PagedAttention
-// deep dive" §2.1; "vLLM inference principles", block-table figure), and
-// query head h reads KV head h / group ("KV-Cache evolution" §3A, GQA).
-//
-// Work decomposition. A workgroup (4 waves) serves one KV head and a run of
-// GH of its query heads, over a range of that KV head's cache blocks: a whole
-// sequence (single pass), one fixed-size partition of a sequence (split
-// context), or an equal share of all blocks of all sequences taken end to end
-// (balanced split: every workgroup reads the same number of blocks, so the
-// grid finishes in one round whatever the length mix). Each K/V byte of the
-// range is read from HBM once and used for all GH heads.
-//
-// Inside a range, the waves take units of NBI blocks round-robin and run
-// independently, each with its own online softmax; the next unit's K/V are
-// loaded into registers while the current one is computed. Per unit:
-//   * logits: one 16x16 MFMA tile per block, rows = query heads (row m holds
-//     head m % GH), columns = the block's 16 tokens, reduced over head_dim in
-//     D/32 steps (16-bit types; fp8 K is first widened exactly to the query's
-//     type) or D/4 steps (fp32). Lane l loads token l%16's row elements
-//     [D/4 * (l/16), +D/4) -- 64 contiguous bytes for bf16 d=128 -- and the
-//     query fragment of each lane covers the same elements, so the product is
-//     the full dot product whatever the MFMA's internal k order;
-//   * online softmax: block max over the 16 token lanes with DPP, running max
-//     m and per-lane partial sums l, rescale alpha = exp2(m_old - m_new);
-//   * P.V on the vector ALU: lane (r, c) of a V load holds 8 elements
-//     [8c, 8c+8) of token row r; the probabilities reach that layout through
-//     a small per-wave LDS buffer; fp32 accumulators acc[head][8].
-// At the end of a range the waves' (m, l, acc) are merged in LDS, in fixed
-// wave order, and written as the output or as one split partial.
-//
-// Masking: tokens at or beyond the range end get a logit of -inf (a select,
-// never a product, so stale or NaN cache contents cannot leak in), and their
-// V words are zeroed before use. Block-table entries past the range end are
-// never read; loads for such blocks are redirected to the range's first block.
-//
-// The arithmetic order depends only on logical token positions (and, in the
-// balanced split, on the context lengths), never on physical block ids:
-// results are bitwise invariant under any relabelling of physical blocks and
-// identical for aliased and private copies of a block.
-
-#include <hip/hip_runtime.h>
-#include <math.h>
+// Decode dispatch (element-type pair, head size, heads per workgroup, split
+// mode) and the merge of split partials, for gfx950. The decode kernels
+// themselves are in pa_decode_kernel.h, instantiated one element-type pair per
+// translation unit.
 
 #include <map>
 #include <mutex>
 #include <utility>
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_decode_kernel.h"
 
 namespace pa {
 namespace {
-
-constexpr int kBs = 16;  // tokens per cache block
-constexpr int kStages = 2;  // register stages of the load pipeline
-// Waves per workgroup (NW below): a fixed partition or a single sequence is
-// split between kFixedWaves waves; a balanced split runs one wide workgroup
-// per compute unit where the registers allow (see balanced_waves).
-constexpr int kFixedWaves = 2;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-struct DecodeParams {
-  void *out;
-  float *tmp_out;
-  float *max_logits;
-  float *exp_sums;
-  const uint8_t *q;
-  const uint8_t *k_cache;
-  const uint8_t *v_cache;
-  const int32_t *block_tables;
-  const int32_t *context_lens;
-  int num_seqs;
-  int num_q_heads;
-  int num_kv_heads;
-  int max_blocks_per_seq;
-  int mode;              // kSplitSingle / kSplitFixed / kSplitBalanced
-  int partition_blocks;  // fixed / single: blocks per partition
-  int max_partitions;    // stride of the partial arrays (see DecodeLaunch)
-  int num_splits;        // balanced: number of shares S
-  int direct;            // a range that is a whole sequence writes `out` directly
-  int group;             // query heads per KV head
-  float scale_log2;      // scale * k_scale * log2(e)
-  float v_scale;
-};
-
-// ---------------------------------------------------------------------------
-// per-type geometry
-// ---------------------------------------------------------------------------
-
-template <int QT, int KT, int D>
-struct Geo {
-  static constexpr int kb = ElemBytes<KT>::value;   // cache element bytes
-  static constexpr int row = D * kb;                // bytes of one head's row
-  // K in the MFMA operand layout: lane l holds token l%16; its piece i is
-  // row bytes k_byte(i, l/16) = [64 i + 16 jq, +16)
-  static constexpr int k_lane_bytes = D / 4 * kb;
-  static constexpr int nkl = k_lane_bytes / 16;     // 16-byte K pieces per lane per block
-  static __device__ __forceinline__ uint32_t k_byte(int i, int jq) { return 64 * i + 16 * jq; }
-  // first element of MFMA step s for lane group jq (8 consecutive elements,
-  // or one for fp32)
-  static __device__ __forceinline__ int q_elem(int s, int jq) {
-    if constexpr (QT == PA_F32) return 16 * (s / 4) + 4 * jq + s % 4;
-    else if constexpr (kb == 1) return 64 * (s / 2) + 16 * jq + 8 * (s % 2);
-    else return 32 * s + 8 * jq;
-  }
-  static constexpr int ksteps = (QT == PA_F32) ? D / 4 : D / 32;  // MFMAs per block
-  // V, accumulate layout: lane (r, c) holds elements [8c, 8c+8) of row r
-  static constexpr int v_piece = 8 * kb;            // bytes per lane per V load
-  static constexpr int lpt = D / 8;                 // lanes per token row
-  static constexpr int rv = kWave / lpt;            // token rows per V load
-  static constexpr int nvl = kBs / rv;              // V loads per lane per block
-  // K global loads are row-contiguous like V (16 bytes per lane, lanes of a
-  // quad on adjacent bytes, so each quad is one cache access): lane (rk, ck)
-  // of load i reads bytes [16 ck, +16) of row i * rvk + rk. The tile then
-  // goes through LDS, rows padded by 16 bytes (the 16 rows of a transposed
-  // read land in distinct banks), into the MFMA operand layout.
-  static constexpr int lpk = row / 16;              // lanes per row of a K load
-  static constexpr int rvk = kWave / lpk;           // rows per K load
-  static constexpr int krs = row + 16;              // LDS row stride of the K tile
-  static_assert(nkl >= 1 && nvl >= 1 && rvk * nkl == kBs, "unsupported geometry");
-};
-
-template <int QT> struct QOpT { using type = u32x4; };  // 8 x 16-bit
-template <> struct QOpT<PA_F32> { using type = float; };
-
-// One V load: 8 cache elements.
-template <int KT> struct VPiece { uint32_t w[2 * ElemBytes<KT>::value]; };
-
-// Buffer resources: the hardware range check of a raw buffer load returns
-// zeros without touching memory for bytes at or beyond num_records, which
-// turns the loads of units past a range's end into no-ops while keeping every
-// load instruction unconditional (one resource per block and cache).
-constexpr int kRsrcFlags = 0x00020000;  // gfx9 word 3: 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes,
-                                           kRsrcFlags);
-}
-
-// K and V are streamed once: loads carry the non-temporal hint (aux bit 1,
-// "nt" on gfx950), which measurably raises the sustained read rate.
-constexpr int kLoadAux = 2;
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux);
-}
-
-template <int KT>
-__device__ __forceinline__ void buf_load_v(VPiece<KT> &pc, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (ElemBytes<KT>::value == 4) {
-    const u32x4 a = buf_load16(r, off);
-    const u32x4 b = buf_load16(r, off + 16);
-    pc.w[0] = a.x; pc.w[1] = a.y; pc.w[2] = a.z; pc.w[3] = a.w;
-    pc.w[4] = b.x; pc.w[5] = b.y; pc.w[6] = b.z; pc.w[7] = b.w;
-  } else if constexpr (ElemBytes<KT>::value == 2) {
-    const u32x4 a = buf_load16(r, off);
-    pc.w[0] = a.x; pc.w[1] = a.y; pc.w[2] = a.z; pc.w[3] = a.w;
-  } else {
-    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadAux);
-    pc.w[0] = a.x; pc.w[1] = a.y;
-  }
-}
-
-// 8 V elements -> fp32; all zero when the token is masked.
-template <int KT>
-__device__ __forceinline__ void widen_v(const VPiece<KT> &pc, bool ok, float (&x)[8]) {
-  constexpr int NW = 2 * ElemBytes<KT>::value;
-  uint32_t w[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = ok ? pc.w[i] : 0u;
-  if constexpr (KT == PA_F32) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = u2f(w[i]);
-  } else if constexpr (KT == PA_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_lo(w[i]);
-      x[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else if constexpr (KT == PA_F16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = f16_lo(w[i]);
-      x[2 * i + 1] = f16_hi(w[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-      x[4 * i] = lo.x;
-      x[4 * i + 1] = lo.y;
-      x[4 * i + 2] = hi.x;
-      x[4 * i + 3] = hi.y;
-    }
-  }
-}
-
-// fp8 pair (bytes 0,1 or 2,3 of a word) widened exactly to the query's 16-bit type
-template <int QT, bool HI>
-__device__ __forceinline__ uint32_t fp8_pair_to_16(uint32_t w) {
-  if constexpr (QT == PA_BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-  }
-}
-
-// B operand of MFMA step s from the lane's K loads of one block.
-template <int QT, int KT, int D>
-__device__ __forceinline__ typename QOpT<QT>::type k_operand(const u32x4 *k, int s) {
-  if constexpr (QT == PA_F32) {
-    const u32x4 w = k[s / 4];
-    const int t = s % 4;
-    return u2f(t == 0 ? w.x : t == 1 ? w.y : t == 2 ? w.z : w.w);
-  } else if constexpr (KT == PA_FP8_E4M3FN) {
-    const u32x4 w = k[s / 2];
-    const uint32_t a = (s % 2) ? w.z : w.x;
-    const uint32_t b = (s % 2) ? w.w : w.y;
-    u32x4 r;
-    r.x = fp8_pair_to_16<QT, false>(a);
-    r.y = fp8_pair_to_16<QT, true>(a);
-    r.z = fp8_pair_to_16<QT, false>(b);
-    r.w = fp8_pair_to_16<QT, true>(b);
-    return r;
-  } else {
-    return k[s];
-  }
-}
-
-template <int QT>
-__device__ __forceinline__ f32x4 mfma(typename QOpT<QT>::type a, typename QOpT<QT>::type b,
-                                      f32x4 c) {
-  if constexpr (QT == PA_BF16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else if constexpr (QT == PA_F16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-}
-
-template <int QT>
-__device__ __forceinline__ void store_elem(void *out, size_t idx, float v) {
-  if constexpr (QT == PA_F32) {
-    static_cast<float *>(out)[idx] = v;
-  } else if constexpr (QT == PA_BF16) {
-    static_cast<uint16_t *>(out)[idx] = f32_to_bf16_rne(v);
-  } else {
-    static_cast<uint16_t *>(out)[idx] = f32_to_f16_rne(v);
-  }
-}
-
-// Orders a wave's LDS accesses (one wave writes and reads its own region;
-// LDS instructions of a wave execute in order, so a compiler fence suffices).
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-
-template <int QT, int KT, int D, int GH, int NBI, int NW>
-struct Shared {
-  float p[NW][NBI * kBs][GH];   // probabilities of the current unit
-  float alpha[NW][GH];          // rescale factor of the current unit
-  float m[NW][GH];              // per-wave softmax state at the end of a range
-  float l[NW][GH];
-  float acc[NW][GH][D];
-  // K tiles of the current unit, one per wave and block
-  uint8_t kt[NW][NBI][kBs * (D * ElemBytes<KT>::value + 16)] __attribute__((aligned(16)));
-  int start[kMaxBalancedSeqs + 1];  // balanced split: first block of each sequence
-  int ctx[kMaxBalancedSeqs];        // balanced split: context length of each sequence
-  int wave_sum[NW];
-  int first[2];  // balanced split: the sequence holding the first block of each share taken
-};
-
-template <int QT, int KT, int D, int GH, int NBI>
-struct Stage {
-  using G = Geo<QT, KT, D>;
-  u32x4 k[NBI][G::nkl];
-  VPiece<KT> v[NBI][G::nvl];
-};
-
-// A range is the blocks [blo, bhi) of sequence b, written as partial
-// `piece` (or to `out` when it is the whole sequence). The units of all
-// ranges of a workgroup are dealt to its waves in turn, counting on across
-// ranges (so the waves' shares of the work differ by one unit at most); a
-// segment is up to kIdsUnits of a wave's units of one range (chunk c), the
-// span one register of block ids covers.
-// A workgroup's work item: the query heads h0 .. h0 + GH - 1 (KV head g)
-// over one balanced share (blocks [lo, hi) of all sequences end to end), or
-// over a single range in the other modes.
-struct Item {
-  int h0, g;
-  int share, lo, hi;
-};
-
-struct Seg {
-  int item;   // work item of the range
-  int h0, g;  // its query heads and KV head
-  int share, ihi;  // balanced: its share and the share's end block
-  int b, blo, bhi, piece;
-  int n;      // context length of sequence b
-  int whole;  // the range is the whole sequence
-  int u0;     // units of the workgroup's earlier ranges
-  int w0;     // this wave's first unit of the range
-  int c;      // chunk of the range
-  int nk;     // this wave's units in the range
-  int kn;     // this wave's units in this segment
-  int last;   // last segment of its range: the range's epilogue follows it
-  int valid;
-};
-
-// All ranges of a workgroup's work items (one range, or the ranges of one
-// or two balanced shares), all waves. The segments of a wave form one
-// pipelined stream: while the last units of a segment are computed, the
-// first unit of the next segment is already being loaded (its block ids and
-// query fragments were fetched one segment ahead), so a switch between
-// ranges costs only the epilogue of the finished range.
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW>
-__device__ __forceinline__ void run_ranges(const DecodeParams &p,
-                                           Shared<QT, KT, D, GH, NBI, NW> &sh, const Item (&items)[2],
-                                           int n_items, int b_first, int n_first, int blo_first,
-                                           int bhi_first, int piece_first, bool whole_first) {
-  using G = Geo<QT, KT, D>;
-  using QOp = typename QOpT<QT>::type;
-  using St = Stage<QT, KT, D, GH, NBI>;
-  constexpr int QB = ElemBytes<QT>::value;
-  constexpr int kIdsUnits = kWave / NBI;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = uniform(tid >> 6);
-  const int jq = lane >> 4;  // MFMA lane group
-  const int tl = lane & 15;  // MFMA column: token within a block
-  const int r = lane / G::lpt;  // V layout: token row within a load
-  const int c = lane % G::lpt;  // V layout: 8-element column group
-  const int Hq = p.num_q_heads;
-  const int B = p.num_seqs;
-  const bool balanced = p.mode == kSplitBalanced;
-
-  // ---- segments ------------------------------------------------------------
-  auto make_seg = [&](int item, const Item &it, int b, int n, int blo, int bhi, int piece,
-                      bool whole, int u0, int ch) {
-    Seg sg;
-    sg.item = item;
-    sg.h0 = it.h0;
-    sg.g = it.g;
-    sg.share = it.share;
-    sg.ihi = it.hi;
-    sg.b = b;
-    sg.n = n;
-    sg.blo = blo;
-    sg.bhi = bhi;
-    sg.piece = piece;
-    sg.whole = whole;
-    sg.u0 = u0;
-    sg.w0 = (wave - u0 % NW + NW) % NW;
-    sg.c = ch;
-    const int nunits = (bhi - blo + NBI - 1) / NBI;
-    sg.nk = sg.w0 < nunits ? (nunits - sg.w0 + NW - 1) / NW : 0;
-    const int nchunks = max(1, (sg.nk + kIdsUnits - 1) / kIdsUnits);
-    sg.kn = max(0, min(kIdsUnits, sg.nk - ch * kIdsUnits));
-    sg.last = ch == nchunks - 1;
-    sg.valid = 1;
-    return sg;
-  };
-  // first chunk of the range of sequence b within balanced item it
-  auto range_seg = [&](int item, const Item &it, int b, int u0) {
-    const int st = uniform(sh.start[b]), en = uniform(sh.start[b + 1]);
-    const int blo = max(it.lo, st) - st, bhi = min(it.hi, en) - st;
-    return make_seg(item, it, b, uniform(sh.ctx[b]), blo, bhi, it.share + b,
-                    blo == 0 && bhi == en - st, u0, 0);
-  };
-  // the segment after sg: the next chunk of its range, else the first chunk
-  // of the next non-empty sequence of the share, else the first range of
-  // the next item
-  auto next_seg = [&](const Seg &sg) {
-    Seg nx = sg;
-    nx.valid = 0;
-    if (!sg.valid) return nx;
-    if (!sg.last) {
-      nx.c = sg.c + 1;
-      nx.kn = max(0, min(kIdsUnits, sg.nk - nx.c * kIdsUnits));
-      nx.last = nx.c == max(1, (sg.nk + kIdsUnits - 1) / kIdsUnits) - 1;
-      nx.valid = 1;
-      return nx;
-    }
-    if (!balanced) return nx;
-    const int u0 = sg.u0 + (sg.bhi - sg.blo + NBI - 1) / NBI;
-    int b = sg.b + 1;
-    while (b < B && sh.start[b] < sg.ihi && sh.start[b + 1] == sh.start[b]) ++b;
-    b = uniform(b);
-    if (b < B && uniform(sh.start[b]) < sg.ihi) {
-      const int st = uniform(sh.start[b]), en = uniform(sh.start[b + 1]);
-      const int bhi = min(sg.ihi, en) - st;
-      Seg r = make_seg(sg.item, Item{sg.h0, sg.g, sg.share, 0, sg.ihi}, b, uniform(sh.ctx[b]), 0,
-                       bhi, sg.share + b, bhi == en - st, u0, 0);
-      return r;
-    }
-    if (sg.item != 0 || n_items < 2) return nx;
-    return range_seg(1, items[1], uniform(sh.first[1]), u0);
-  };
-  // lane i: physical id of block i % NBI of the segment's unit i / NBI
-  auto fetch_ids = [&](const Seg &sg) {
-    const int kk = sg.c * kIdsUnits + lane / NBI;
-    const int j = sg.blo + (sg.w0 + kk * NW) * NBI + lane % NBI;
-    const bool ok = sg.valid && kk < sg.nk && j < sg.bhi;
-    const int32_t *row = p.block_tables + (size_t)(sg.valid ? sg.b : 0) * p.max_blocks_per_seq;
-    return row[ok ? j : 0];
-  };
-  // query fragments (A operand) of sequence b: row tl holds head h0 + tl % GH
-  auto load_q = [&](int b, int h0, QOp (&qa)[G::ksteps]) {
-    const uint8_t *qrow = p.q + ((size_t)b * Hq + h0 + tl % GH) * D * QB;
-    if constexpr (QT == PA_F32) {
-      const float *qf = reinterpret_cast<const float *>(qrow);
-#pragma unroll
-      for (int s = 0; s < G::ksteps; s += 4) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(qf + G::q_elem(s, jq));
-        qa[s] = u2f(w.x);
-        qa[s + 1] = u2f(w.y);
-        qa[s + 2] = u2f(w.z);
-        qa[s + 3] = u2f(w.w);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < G::ksteps; ++s)
-        qa[s] = *reinterpret_cast<const u32x4 *>(qrow + G::q_elem(s, jq) * QB);
-    }
-  };
-
-  // ---- per-wave softmax state ----------------------------------------------
-  float m[4], l[4];
-  float acc[GH][8];
-  auto reset = [&]() {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      m[v] = -INFINITY;
-      l[v] = 0.0f;
-    }
-#pragma unroll
-    for (int h = 0; h < GH; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-  };
-
-  const uint32_t rowstride = (uint32_t)p.num_kv_heads * G::row;
-  const uint32_t blk_bytes = rowstride * kBs;          // < 2^31, checked on the host
-  const uint32_t k_off = (lane / G::lpk) * rowstride + (lane % G::lpk) * 16;
-  uint32_t v_off[G::nvl];
-#pragma unroll
-  for (int i = 0; i < G::nvl; ++i) v_off[i] = (i * G::rv + r) * rowstride + c * G::v_piece;
-  const float sl2 = p.scale_log2;
-
-  // Loads of one unit of KV head g into a register stage: the unit whose
-  // block ids start at lane u * NBI of `ids`; an invalid unit loads nothing.
-  auto issue = [&](int ids, int u, bool valid, int g, St &st) {
-    // head g's row 0 to the block end
-    const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;
-#pragma unroll
-    for (int bi = 0; bi < NBI; ++bi) {
-      const int lidx = min(u * NBI + bi, kWave - 1);
-      const int id = __builtin_amdgcn_readlane(ids, lidx);
-      const size_t off = (size_t)id * blk_bytes + (size_t)g * G::row;
-      const uint32_t n = valid ? blk_span : 0u;
-      const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.k_cache + off, n);
-      const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.v_cache + off, n);
-#pragma unroll
-      for (int i = 0; i < G::nkl; ++i) st.k[bi][i] = buf_load16(rk, k_off + i * G::rvk * rowstride);
-#pragma unroll
-      for (int i = 0; i < G::nvl; ++i) buf_load_v<KT>(st.v[bi][i], rv, v_off[i]);
-    }
-  };
-
-  auto compute_unit = [&](int jb, int tok_lim, const QOp (&qa)[G::ksteps], const St &st) {
-    // logits, log2 domain; masked tokens -inf
-    float sv[NBI][4];
-    // K tile: registers (row-contiguous) -> LDS -> MFMA operand layout, in
-    // which lane (tl, jq) holds bytes k_byte(i, jq) of token row tl
-#pragma unroll
-    for (int bi = 0; bi < NBI; ++bi)
-#pragma unroll
-      for (int i = 0; i < G::nkl; ++i)
-        *reinterpret_cast<u32x4 *>(&sh.kt[wave][bi][(i * G::rvk + lane / G::lpk) * G::krs +
-                                                    (lane % G::lpk) * 16]) = st.k[bi][i];
-    wave_lds_fence();
-#pragma unroll
-    for (int bi = 0; bi < NBI; ++bi) {
-      u32x4 kop[G::nkl];
-#pragma unroll
-      for (int i = 0; i < G::nkl; ++i)
-        kop[i] = *reinterpret_cast<const u32x4 *>(&sh.kt[wave][bi][tl * G::krs + G::k_byte(i, jq)]);
-      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < G::ksteps; ++s) d = mfma<QT>(qa[s], k_operand<QT, KT, D>(kop, s), d);
-      const bool ok = (jb + bi) * kBs + tl < tok_lim;
-      sv[bi][0] = ok ? d.x * sl2 : -INFINITY;
-      sv[bi][1] = ok ? d.y * sl2 : -INFINITY;
-      sv[bi][2] = ok ? d.z * sl2 : -INFINITY;
-      sv[bi][3] = ok ? d.w * sl2 : -INFINITY;
-    }
-    // online softmax per MFMA row v (head (4*jq + v) % GH)
-    float al[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float mx = sv[0][v];
-#pragma unroll
-      for (int bi = 1; bi < NBI; ++bi) mx = fmaxf(mx, sv[bi][v]);
-      mx = group_max<16>(mx);
-      const float mn = fmaxf(m[v], mx);
-      al[v] = __builtin_amdgcn_exp2f(m[v] - mn);
-      m[v] = mn;
-      float sum = 0.0f;
-#pragma unroll
-      for (int bi = 0; bi < NBI; ++bi) {
-        const float e = __builtin_amdgcn_exp2f(sv[bi][v] - mn);
-        sv[bi][v] = e;
-        sum += e;
-      }
-      l[v] = l[v] * al[v] + sum;
-    }
-    // hand the probabilities and alpha to the V layout
-    if (4 * jq < GH) {
-#pragma unroll
-      for (int bi = 0; bi < NBI; ++bi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (v < GH) sh.p[wave][bi * kBs + tl][4 * jq + v] = sv[bi][v];
-      if (tl == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (v < GH) sh.alpha[wave][4 * jq + v] = al[v];
-      }
-    }
-    wave_lds_fence();
-    {
-      float a[GH];
-#pragma unroll
-      for (int h = 0; h < GH; ++h) a[h] = sh.alpha[wave][h];
-#pragma unroll
-      for (int h = 0; h < GH; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= a[h];
-    }
-#pragma unroll
-    for (int bi = 0; bi < NBI; ++bi) {
-#pragma unroll
-      for (int i = 0; i < G::nvl; ++i) {
-        const int t = i * G::rv + r;
-        const bool ok = (jb + bi) * kBs + t < tok_lim;
-        float x[8];
-        widen_v<KT>(st.v[bi][i], ok, x);
-        float pw[GH];
-#pragma unroll
-        for (int h = 0; h < GH; ++h) pw[h] = sh.p[wave][bi * kBs + t][h];
-#pragma unroll
-        for (int h = 0; h < GH; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], x[e], acc[h][e]);
-      }
-    }
-    wave_lds_fence();
-  };
-
-  // end of a range: merge the waves' softmax states and write the range's
-  // partial (or the output, for a whole sequence)
-  auto epilogue = [&](int b, int piece, bool whole, int h0) {
-    // merge the waves: sums over the token lanes / rows, then across waves
-  #pragma unroll
-    for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
-    if (4 * jq < GH && tl == 0) {
-  #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (v < GH) {
-          sh.m[wave][4 * jq + v] = m[v];
-          sh.l[wave][4 * jq + v] = l[v];
-        }
-    }
-  #pragma unroll
-    for (int h = 0; h < GH; ++h)
-  #pragma unroll
-      for (int e = 0; e < 8; ++e)
-  #pragma unroll
-        for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
-    if (r == 0) {
-  #pragma unroll
-      for (int h = 0; h < GH; ++h)
-  #pragma unroll
-        for (int e = 0; e < 8; ++e) sh.acc[wave][h][c * 8 + e] = acc[h][e];
-    }
-    __syncthreads();
-
-    const bool to_out = whole && p.direct;
-    for (int i = tid; i < GH * D; i += (NW * kWave)) {
-      const int h = i / D, d = i % D;
-      float M = -INFINITY;
-  #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sh.m[w][h]);
-      float L = 0.0f, O = 0.0f;
-  #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float sc = __builtin_amdgcn_exp2f(sh.m[w][h] - M);
-        L += sh.l[w][h] * sc;
-        O += sh.acc[w][h][d] * sc;
-      }
-      const float res = O * p.v_scale / L;
-      const size_t bh = (size_t)b * Hq + h0 + h;
-      if (to_out) {
-        store_elem<QT>(p.out, bh * D + d, res);
-      } else {
-        const size_t pi = (p.mode == kSplitBalanced)
-                              ? (size_t)(h0 + h) * p.max_partitions + piece
-                              : bh * p.max_partitions + piece;
-        p.tmp_out[pi * D + d] = res;
-        if (d == 0) {
-          p.max_logits[pi] = M * kLn2;
-          p.exp_sums[pi] = L;
-        }
-      }
-    }
-    __syncthreads();
-  };
-
-  // ---- the stream ------------------------------------------------------------
-  Seg cur = make_seg(0, items[0], b_first, n_first, blo_first, bhi_first, piece_first,
-                     whole_first, 0, 0);
-  // the first segment's loads go out before the LDS walk to the next one
-  int ids_cur = fetch_ids(cur);
-  QOp q_cur[G::ksteps], q_nxt[G::ksteps];
-  load_q(cur.b, items[0].h0, q_cur);
-  Seg nxt = next_seg(cur);
-  St st[NS];
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(ids_cur, s, s < cur.kn, cur.g, st[s]);
-  int ids_nxt = fetch_ids(nxt);
-  load_q(nxt.valid ? nxt.b : cur.b, nxt.valid ? nxt.h0 : cur.h0, q_nxt);
-  reset();
-  for (;;) {
-    // Units k = 0 .. kn-1 of the segment through NS register stages in turn:
-    // while unit k is computed, the loads of units k+1 .. k+NS-1 are in
-    // flight; indices from kpad on are the next segment's first units, which
-    // land in the stages its own loop starts from. Every load instruction is
-    // issued unconditionally (past the end they read nothing), so the
-    // compiler's memory-counter waits stay exact: computing a unit waits only
-    // for that unit.
-    const int kn = cur.kn;
-    const int kpad = max(NS, (kn + NS - 1) / NS * NS);
-    const int g_cur = cur.g, g_nxt = nxt.valid ? nxt.g : cur.g;
-    const int jb0 = cur.blo + (cur.w0 + cur.c * kIdsUnits * NW) * NBI;
-    const int tok_lim = min(cur.bhi * kBs, cur.n);
-    for (int k = 0; k < kpad - NS; k += NS) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int u = k + s + NS - 1;
-        issue(ids_cur, u, u < kn, g_cur, st[(s + NS - 1) % NS]);
-        if (k + s < kn) compute_unit(jb0 + (k + s) * NW * NBI, tok_lim, q_cur, st[s]);
-      }
-    }
-    // the last step, peeled: it issues this segment's last unit and the
-    // next segment's first NS - 1 units (so that the ids of the next
-    // segment are read only here, where their load is long done)
-    {
-      const int k = kpad - NS;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s == 0) issue(ids_cur, kpad - 1, kpad - 1 < kn, g_cur, st[NS - 1]);
-        else issue(ids_nxt, s - 1, nxt.valid && s - 1 < nxt.kn, g_nxt, st[s - 1]);
-        if (k + s < kn) compute_unit(jb0 + (k + s) * NW * NBI, tok_lim, q_cur, st[s]);
-      }
-    }
-    // move to the next segment (copies of loads issued a segment ago, made
-    // before the epilogue's stores so that their waits do not cover the
-    // next segment's loads already in flight)
-    const Seg done = cur;
-    cur = nxt;
-    ids_cur = ids_nxt;
-#pragma unroll
-    for (int s = 0; s < G::ksteps; ++s) q_cur[s] = q_nxt[s];
-    if (done.last) {
-      epilogue(done.b, done.piece, done.whole, done.h0);
-      reset();
-    }
-    if (!cur.valid) break;
-    nxt = next_seg(cur);
-    ids_nxt = fetch_ids(nxt);
-    load_q(nxt.valid ? nxt.b : cur.b, nxt.valid ? nxt.h0 : cur.h0, q_nxt);
-  }
-}
-
-__device__ __forceinline__ int num_blocks_of(int n) { return n > 0 ? (n + kBs - 1) / kBs : 0; }
-
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
-  __shared__ Shared<QT, KT, D, GH, NBI, NW> sh;
-  const int tid = threadIdx.x;
-
-  Item items[2];
-  int n_items = 1;
-  // the first range: blocks [first_lo, first_hi) of sequence first_b
-  int first_b = 0, first_n = 0, first_lo = 0, first_hi = 0, first_piece = 0;
-  bool first_whole = false;
-  if (p.mode != kSplitBalanced) {
-    const int h0 = blockIdx.y * GH;  // first query head of this workgroup
-    const int b = blockIdx.z;
-    const int part = blockIdx.x;
-    const int n = p.context_lens[b];
-    if (n <= 0) {
-      if (p.mode == kSplitSingle)
-        for (int i = tid; i < GH * D; i += (NW * kWave))
-          store_elem<QT>(p.out, ((size_t)b * p.num_q_heads + h0) * D + i, 0.0f);
-      return;
-    }
-    const int nblk = num_blocks_of(n);
-    const int blo = part * p.partition_blocks;
-    if (blo >= nblk) return;
-    items[0] = Item{h0, h0 / p.group, 0, 0, 0};
-    first_b = b;
-    first_n = n;
-    first_lo = blo;
-    first_hi = min(nblk, blo + p.partition_blocks);
-    first_piece = part;
-    first_whole = nblk <= p.partition_blocks;
-  } else {
-    // Balanced split: the blocks of all sequences, end to end, cut into
-    // num_splits equal shares. First the start block of every sequence
-    // (exclusive prefix sum of ceil(n / 16)).
-    const int B = p.num_seqs;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    {
-      constexpr int PER = kMaxBalancedSeqs / (NW * kWave);
-      int cnt[PER];
-      int tot = 0;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int bb = PER * tid + k;
-        const int n = bb < B ? p.context_lens[bb] : 0;
-        if (bb < B) sh.ctx[bb] = n;
-        cnt[k] = num_blocks_of(n);
-        tot += cnt[k];
-      }
-      int incl = tot;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      if (lane == kWave - 1) sh.wave_sum[wave] = incl;
-      __syncthreads();
-      int base = 0, all = 0;
-      for (int w = 0; w < NW; ++w) {
-        const int ws = sh.wave_sum[w];
-        if (w < wave) base += ws;
-        all += ws;
-      }
-      // the first blocks of this workgroup's shares (see below), and the
-      // sequences holding them: each thread checks its own sequences
-      const int S = min(p.num_splits, all);
-      const int s0 = 2 * blockIdx.x;
-      const long long f0 = s0 < S ? (long long)s0 * all / S : -1;
-      const long long f1 = s0 + 1 < S ? (long long)(s0 + 1) * all / S : -1;
-      int ex = base + incl - tot;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int bb = PER * tid + k;
-        if (bb < B) sh.start[bb] = ex;
-        if (ex <= f0 && f0 < ex + cnt[k]) sh.first[0] = bb;
-        if (ex <= f1 && f1 < ex + cnt[k]) sh.first[1] = bb;
-        ex += cnt[k];
-      }
-      if (tid == (NW * kWave) - 1) sh.start[B] = base + incl;
-      __syncthreads();
-    }
-    const int total = uniform(sh.start[B]);
-    // at most one share per block, so that no share is empty
-    const int S = min(p.num_splits, total);
-    // Workgroup (x, y) takes share 2x of its own head row y and share 2x + 1
-    // of the paired row y ^ 1 (the pair's other workgroup takes the other
-    // two). The cache rows of neighbouring KV heads sit in different halves
-    // of the memory interleave, which the hardware serves at different
-    // rates; pairing gives every workgroup the same mix.
-    const int y = blockIdx.y;
-    const int y2 = (y ^ 1) < (int)gridDim.y ? (y ^ 1) : y;
-    const int s0 = 2 * blockIdx.x;
-    if (s0 >= S) return;
-    n_items = s0 + 1 < S ? 2 : 1;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int s = min(s0 + k, S - 1);
-      const int h0 = (k == 0 ? y : y2) * GH;
-      items[k] = Item{h0, h0 / p.group, s, (int)((long long)s * total / S),
-                      (int)((long long)(s + 1) * total / S)};
-    }
-    first_b = uniform(sh.first[0]);
-    const int st = uniform(sh.start[first_b]), en = uniform(sh.start[first_b + 1]);
-    first_n = uniform(sh.ctx[first_b]);
-    first_lo = items[0].lo - st;
-    first_hi = min(items[0].hi, en) - st;
-    first_piece = items[0].share + first_b;
-    first_whole = first_lo == 0 && first_hi == en - st;
-  }
-  run_ranges<QT, KT, D, GH, NBI, NS, NW>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
-                                     first_piece, first_whole);
-}
 
 // ---------------------------------------------------------------------------
 // merge of split partials
@@ -939,75 +134,18 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
   store_elem<OT>(p.out, bh * D + d, O / W);
 }
 
-// ---------------------------------------------------------------------------
-// dispatch
-// ---------------------------------------------------------------------------
-
-template <int QT, int KT, int GH>
-constexpr int units_of() {
-  // blocks per unit: two for fp8 caches with up to 4 heads per workgroup
-  // (64 bytes of K and V per lane per block), one otherwise -- two register
-  // stages of one unit each stay within 256 VGPRs
-  return (ElemBytes<KT>::value == 1 && GH <= 4) ? 2 : 1;
-}
-
-
-// Waves of a balanced-split workgroup: eight (one workgroup per compute
-// unit: the hardware serves the workgroups of a compute unit unevenly, the
-// waves of one workgroup alike) where two waves per SIMD fit the registers
-// without spills, else four.
-template <int QT, int KT, int D, int GH>
-constexpr int balanced_waves() {
-  if (GH > 8) return 4;
-  if (QT == PA_F32) return (D == 64 || GH == 1) ? 8 : 4;
-  return 8;
-}
-
-struct KernelRef {
-  const void *fn;
-  int threads;
-};
-
-template <int QT, int KT, int D, int GH>
-KernelRef kernel_of(bool balanced) {
-  constexpr int NBI = units_of<QT, KT, GH>();
-  constexpr int NWB = balanced_waves<QT, KT, D, GH>();
-  if (balanced)
-    return {reinterpret_cast<const void *>(&decode_kernel<QT, KT, D, GH, NBI, kStages, NWB>),
-            NWB * kWave};
-  return {reinterpret_cast<const void *>(&decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves>),
-          kFixedWaves * kWave};
-}
-
-template <int QT, int KT, int D>
-KernelRef by_gh(int gh, bool balanced) {
-  switch (gh) {
-    case 1: return kernel_of<QT, KT, D, 1>(balanced);
-    case 2: return kernel_of<QT, KT, D, 2>(balanced);
-    case 4: return kernel_of<QT, KT, D, 4>(balanced);
-    case 8: return kernel_of<QT, KT, D, 8>(balanced);
-    case 16: return kernel_of<QT, KT, D, 16>(balanced);
-  }
-  return {nullptr, 0};
-}
-
-template <int QT, int KT>
-KernelRef by_d(int d, int gh, bool balanced) {
-  switch (d) {
-    case 64: return by_gh<QT, KT, 64>(gh, balanced);
-    case 128: return by_gh<QT, KT, 128>(gh, balanced);
-  }
-  return {nullptr, 0};
-}
-
-KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, bool balanced) {
-  if (q_dtype == PA_F32 && kv_dtype == PA_F32) return by_d<PA_F32, PA_F32>(d, gh, balanced);
-  if (q_dtype == PA_F16 && kv_dtype == PA_F16) return by_d<PA_F16, PA_F16>(d, gh, balanced);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) return by_d<PA_BF16, PA_BF16>(d, gh, balanced);
+KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, bool balanced,
+                            bool append) {
+  if (q_dtype == PA_F32 && kv_dtype == PA_F32)
+    return decode_kernels_f32_f32(d, gh, balanced, append);
+  if (q_dtype == PA_F16 && kv_dtype == PA_F16)
+    return decode_kernels_f16_f16(d, gh, balanced, append);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16)
+    return decode_kernels_bf16_bf16(d, gh, balanced, append);
   if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN)
-    return by_d<PA_F16, PA_FP8_E4M3FN>(d, gh, balanced);
+    return decode_kernels_f16_fp8(d, gh, balanced, append);
   if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN)
-    return by_d<PA_BF16, PA_FP8_E4M3FN>(d, gh, balanced);
+    return decode_kernels_bf16_fp8(d, gh, balanced, append);
   return {nullptr, 0};
 }
 
@@ -1041,7 +179,7 @@ int fill_workgroups(const void *fn, int threads) {
 
 int balanced_num_splits(const DecodeLaunch &a) {
   const int gh = heads_per_workgroup(a.num_q_heads / a.num_kv_heads);
-  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, true);
+  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, true, false);
   if (!k.fn) return 2;
   const int cus = fill_workgroups(k.fn, k.threads);
   if (cus <= 0) return kMaxAutoSplits / 8;
@@ -1078,9 +216,15 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   const float ks = a.kv_dtype == PA_FP8_E4M3FN ? a.k_scale : 1.0f;
   p.scale_log2 = a.scale * ks * kLog2e;
   p.v_scale = a.kv_dtype == PA_FP8_E4M3FN ? a.v_scale : 1.0f;
+  p.new_k = static_cast<const uint8_t *>(a.new_k);
+  p.new_v = static_cast<const uint8_t *>(a.new_v);
+  p.k_cache_w = const_cast<uint8_t *>(p.k_cache);
+  p.v_cache_w = const_cast<uint8_t *>(p.v_cache);
+  p.k_scale = a.k_scale;
+  p.v_scale_w = a.v_scale;
   const int gh = heads_per_workgroup(p.group);
-  const KernelRef k =
-      decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, a.mode == kSplitBalanced);
+  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh,
+                                        a.mode == kSplitBalanced, a.new_k != nullptr);
   if (!k.fn) return (int)hipErrorInvalidValue;
   const int head_groups = a.num_kv_heads * (p.group / gh);
   dim3 grid;

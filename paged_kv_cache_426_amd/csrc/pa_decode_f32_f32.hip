@@ -1,0 +1,11 @@
+// Decode kernels for float32 queries and float32 caches.
+
+#include "pa_decode_kernel.h"
+
+namespace pa {
+
+KernelRef decode_kernels_f32_f32(int d, int gh, bool balanced, bool append) {
+  return by_d<PA_F32, PA_F32>(d, gh, balanced, append);
+}
+
+}  // namespace pa

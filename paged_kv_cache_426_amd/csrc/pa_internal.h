@@ -43,6 +43,11 @@ struct DecodeLaunch {
   int partition_size;  // fixed split: tokens per partition
   int num_splits;      // balanced split: shares
   int direct;          // a range covering a whole sequence writes `out` directly
+  // decode with append: the new token of every sequence (position n - 1),
+  // [num_seqs, Hkv, d] in q's type, written to its slot and attended from
+  // these rows; null for a plain decode
+  const void *new_k;
+  const void *new_v;
 };
 
 struct ReduceLaunch {
@@ -58,6 +63,12 @@ struct ReduceLaunch {
   int num_splits;      // balanced
   int skip_single;     // sequences held in one piece were already written
   int out_dtype;
+};
+
+// A decode kernel's host-side handle and the workgroup size it is built for.
+struct KernelRef {
+  const void *fn;
+  int threads;
 };
 
 // Each returns 0 on success or the runtime's error code.

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("pa_decode", "pa_decode_partials", "pa_decode_reduce",
+    for required in ("pa_decode", "pa_decode_append", "pa_decode_partials", "pa_decode_reduce",
                      "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_size",
                      "pa_num_partitions", "pa_status_string", "pa_version"):
         assert required in names
@@ -99,6 +99,30 @@ def test_decode_validation(kw, status):
 
 def test_zero_sequences_is_a_no_op():
     assert _decode(B=0) == 0
+
+
+def _append(**kw):
+    args = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=2,
+                Hq=4, Hkv=2, d=64, bs=16, NB=16, MBS=4, scale=0.125, qt=pa.PA_BF16,
+                kt=pa.PA_BF16, ks=1.0, vs=1.0, P=0, ws=NULL, wsb=0, stream=NULL)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_decode_append(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"],
+                                     a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["bs"],
+                                     a["NB"], a["MBS"], a["scale"], a["qt"], a["kt"], a["ks"],
+                                     a["vs"], a["P"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=NULL), 1), (dict(value=NULL), 1), (dict(out=NULL), 1), (dict(k=NULL), 1),
+    (dict(kt=pa.PA_FP8_E4M3FN, ks=0.0), 2),        # the new rows are quantised: scale != 0
+    (dict(kt=pa.PA_FP8_E4M3FN, vs=float("nan")), 2),
+    (dict(Hq=3), 2), (dict(d=96), 3),
+    (dict(P=16), 1),                               # split without workspace
+    (dict(B=0), 0),                                # no sequences: no-op
+])
+def test_decode_append_validation(kw, status):
+    assert _append(**kw) == status
 
 
 def test_partials_and_reduce_validation():
