@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partition-size P] [--layers L] [--no-cpu-baseline]
+                    [--block-size BS] [--placement permuted|contiguous]
 
 One step is one pass of the whole decode hot path over one batch of synthetic
 input, on one attention layer: the copy-on-write block copies the workload
@@ -53,6 +54,10 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per cache block (Llama-shaped workload only; default 16)")
+    ap.add_argument("--placement", choices=("permuted", "contiguous"), default=None,
+                    help="physical block order (Llama-shaped workload only; default permuted)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="tokens per split-context partition (0 = single pass); "
                          "default: the workload's own launch configuration")
@@ -248,6 +253,10 @@ def main(argv=None):
 
     t0 = time.perf_counter()
     kw = {} if args.partition_size is None else {"partition_size": args.partition_size}
+    if args.block_size is not None:
+        kw["block_size"] = args.block_size
+    if args.placement is not None:
+        kw["placement"] = args.placement
     wl = W.build(args.workload, **kw)
     P = wl.partition_size
     log(f"workload {wl.name}: B={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
@@ -420,6 +429,7 @@ def main(argv=None):
             "num_kv_heads": wl.num_kv_heads,
             "head_dim": wl.head_dim,
             "block_size": wl.block_size,
+            "placement": args.placement or "permuted",
             "num_blocks": wl.num_blocks,
             "q_dtype": wl.q_dtype,
             "kv_dtype": wl.kv_dtype,

@@ -42,9 +42,14 @@
  *     result is undefined.
  *   - A launch failure reported by the runtime returns PA_ERR_LAUNCH.
  *
- * Supported configurations: head_dim 64 or 128; block_size 16; any
- * num_q_heads that is a multiple of num_kv_heads; (q, kv) element types
- * (f32, f32), (f16, f16), (bf16, bf16), (f16, fp8_e4m3fn), (bf16, fp8_e4m3fn).
+ * Supported configurations: head_dim 64 or 128; block_size 16, 32, 64, 128
+ * or 256 for decode (the pages give 16 as the usual size and suggest 16 to
+ * 128, or 64 to 256: "PagedAttention deep dive" section 2.1, "KV-cache
+ * sharing article" sections 2 and 4), any block size for the slot write and
+ * the block copy; any num_q_heads that is a multiple of num_kv_heads; (q, kv)
+ * element types (f32, f32), (f16, f16), (bf16, bf16), (f16, fp8_e4m3fn),
+ * (bf16, fp8_e4m3fn). Decode reads a block of 16 * 2^k tokens as 2^k
+ * consecutive 16-token sub-blocks.
  */
 #ifndef PA_H
 #define PA_H
@@ -86,9 +91,10 @@ int pa_version(void);
  *   0      single pass: one workgroup reads a sequence's whole context.
  *   P > 0  fixed split: partition p of sequence b covers logical tokens
  *          [p*P, min((p+1)*P, n)); P is a multiple of block_size.
- *   -S     balanced split with S >= 2 shares: the cache blocks of all
- *          sequences, taken end to end in sequence order (ceil(n_b / 16)
- *          blocks for sequence b, T in total), are cut into S shares, share
+ *   -S     balanced split with S >= 2 shares: the 16-token sub-blocks of
+ *          all sequences (whatever the block size), taken end to end in
+ *          sequence order (ceil(n_b / 16) of them for sequence b, T in
+ *          total), are cut into S shares, share
  *          s being blocks [floor(s*T/S), floor((s+1)*T/S)) (S is first
  *          clamped to T). Each piece = (share, sequence) intersection is one
  *          partial; every share holds the same number of blocks, so the work

@@ -191,10 +191,13 @@ def balanced_pieces(context_lens, block_size, num_splits):
 
 
 def paged_decode_pieces(q, k_cache, v_cache, block_tables, context_lens, scale, pieces,
-                        k_scale=1.0, v_scale=1.0):
+                        k_scale=1.0, v_scale=1.0, unit=None):
     """(m, l, o~) of each piece (s, b, first_block, end_block) for every query
     head: the softmax statistics of the piece's own tokens
-    [first_block * bs, min(end_block * bs, n)), as in paged_decode_partials.
+    [first_block * u, min(end_block * u, n)), as in paged_decode_partials,
+    where u = unit, the number of tokens the piece bounds count in (the
+    cache's block size unless given; the library's balanced split counts
+    16-token sub-blocks whatever the block size).
     Shapes: m, l [len(pieces), Hq]; o~ [len(pieces), Hq, d]."""
     q64 = to_f64(q)
     B, Hq, d = q64.shape
@@ -212,7 +215,8 @@ def paged_decode_pieces(q, k_cache, v_cache, block_tables, context_lens, scale, 
         ids = np.asarray(block_tables[b][:nblk], dtype=np.int64)
         K = gather_logical_kv(to_f64(k_cache[ids]), np.arange(nblk), n) * ks
         V = gather_logical_kv(to_f64(v_cache[ids]), np.arange(nblk), n) * vs
-        lo, hi = fb * bs, min(eb * bs, n)
+        u = bs if unit is None else int(unit)
+        lo, hi = fb * u, min(eb * u, n)
         for h in range(Hq):
             g = h // group
             sc = (K[lo:hi, g, :] @ q64[b, h]) * scale64

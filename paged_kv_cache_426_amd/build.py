@@ -21,9 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_cache.hip", "pa_decode_f32_f32.hip",
-           "pa_decode_f16_f16.hip", "pa_decode_bf16_bf16.hip", "pa_decode_f16_fp8.hip",
-           "pa_decode_bf16_fp8.hip"]
+PAIRS = ["f32_f32", "f16_f16", "bf16_bf16", "f16_fp8", "bf16_fp8"]
+SOURCES = (["pa_api.cpp", "pa_decode.hip", "pa_cache.hip"] +
+           [f"pa_decode_{p}.hip" for p in PAIRS] + [f"pa_decode_{p}_large.hip" for p in PAIRS])
 
 ARCH = "gfx950"
 

@@ -10,8 +10,6 @@
 
 namespace {
 
-constexpr int kSupportedBlockSize = 16;
-
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 bool known_dtype(int t) {
@@ -39,7 +37,7 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
     return PA_ERR_BAD_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
   if (!known_dtype(q_dtype) || !known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
-  if (!supported_head_dim(head_dim) || block_size != kSupportedBlockSize ||
+  if (!supported_head_dim(head_dim) || pa::sub_block_log2(block_size) < 0 ||
       !supported_decode_pair(q_dtype, kv_dtype))
     return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
@@ -55,6 +53,8 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
   if (grid_y > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   if (partition_size < -pa::kMaxAutoSplits) return PA_ERR_UNSUPPORTED;
   if ((long long)max_blocks_per_seq * block_size > INT_MAX) return PA_ERR_UNSUPPORTED;
+  // the kernels address the pool in 16-token sub-blocks with 32-bit ids
+  if ((long long)num_blocks * (block_size / 16) > INT_MAX) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 

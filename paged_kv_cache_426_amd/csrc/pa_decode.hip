@@ -135,17 +135,22 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
 }
 
 KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, bool balanced,
-                            bool append) {
+                            bool append, bool large) {
   if (q_dtype == PA_F32 && kv_dtype == PA_F32)
-    return decode_kernels_f32_f32(d, gh, balanced, append);
+    return large ? decode_kernels_f32_f32_large(d, gh, balanced, append)
+                 : decode_kernels_f32_f32(d, gh, balanced, append);
   if (q_dtype == PA_F16 && kv_dtype == PA_F16)
-    return decode_kernels_f16_f16(d, gh, balanced, append);
+    return large ? decode_kernels_f16_f16_large(d, gh, balanced, append)
+                 : decode_kernels_f16_f16(d, gh, balanced, append);
   if (q_dtype == PA_BF16 && kv_dtype == PA_BF16)
-    return decode_kernels_bf16_bf16(d, gh, balanced, append);
+    return large ? decode_kernels_bf16_bf16_large(d, gh, balanced, append)
+                 : decode_kernels_bf16_bf16(d, gh, balanced, append);
   if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN)
-    return decode_kernels_f16_fp8(d, gh, balanced, append);
+    return large ? decode_kernels_f16_fp8_large(d, gh, balanced, append)
+                 : decode_kernels_f16_fp8(d, gh, balanced, append);
   if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN)
-    return decode_kernels_bf16_fp8(d, gh, balanced, append);
+    return large ? decode_kernels_bf16_fp8_large(d, gh, balanced, append)
+                 : decode_kernels_bf16_fp8(d, gh, balanced, append);
   return {nullptr, 0};
 }
 
@@ -179,7 +184,8 @@ int fill_workgroups(const void *fn, int threads) {
 
 int balanced_num_splits(const DecodeLaunch &a) {
   const int gh = heads_per_workgroup(a.num_q_heads / a.num_kv_heads);
-  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, true, false);
+  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, true, false,
+                                        false);
   if (!k.fn) return 2;
   const int cus = fill_workgroups(k.fn, k.threads);
   if (cus <= 0) return kMaxAutoSplits / 8;
@@ -206,11 +212,15 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.max_blocks_per_seq = a.max_blocks_per_seq;
+  // the kernels count 16-token sub-blocks; block_size is 16 << sub_log2
+  p.sub_log2 = sub_block_log2(a.block_size);
+  if (p.sub_log2 < 0) return (int)hipErrorInvalidValue;
   p.mode = a.mode;
-  p.partition_blocks = a.mode == kSplitSingle ? a.max_blocks_per_seq
-                                              : a.partition_size / a.block_size;
+  p.partition_blocks = a.mode == kSplitSingle ? a.max_blocks_per_seq << p.sub_log2
+                                              : a.partition_size / kBs;
   p.max_partitions = a.max_partitions;
   p.num_splits = a.num_splits;
+  const bool wide = p.mode == kSplitBalanced;
   p.direct = a.direct;
   p.group = a.num_q_heads / a.num_kv_heads;
   const float ks = a.kv_dtype == PA_FP8_E4M3FN ? a.k_scale : 1.0f;
@@ -223,12 +233,12 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.k_scale = a.k_scale;
   p.v_scale_w = a.v_scale;
   const int gh = heads_per_workgroup(p.group);
-  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh,
-                                        a.mode == kSplitBalanced, a.new_k != nullptr);
+  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, wide,
+                                        a.new_k != nullptr, p.sub_log2 > 0);
   if (!k.fn) return (int)hipErrorInvalidValue;
   const int head_groups = a.num_kv_heads * (p.group / gh);
   dim3 grid;
-  if (a.mode == kSplitBalanced) grid = dim3((a.num_splits + 1) / 2, head_groups, 1);
+  if (wide) grid = dim3((p.num_splits + 1) / 2, head_groups, 1);
   else if (a.mode == kSplitFixed) grid = dim3(a.max_partitions, head_groups, a.num_seqs);
   else grid = dim3(1, head_groups, a.num_seqs);
   void *args[] = {&p};
@@ -249,7 +259,7 @@ int launch_reduce(const ReduceLaunch &a, void *stream) {
   p.num_q_heads = a.num_q_heads;
   p.max_partitions = a.max_partitions;
   p.mode = a.mode;
-  p.partition_blocks = a.mode == kSplitFixed ? a.partition_size / a.block_size : 0;
+  p.partition_blocks = a.mode == kSplitFixed ? a.partition_size / kBs : 0;
   p.num_splits = a.num_splits;
   p.skip_single = a.skip_single;
   const int hpw = kReduceThreads / a.head_dim;

@@ -5,7 +5,7 @@
 namespace pa {
 
 KernelRef decode_kernels_bf16_bf16(int d, int gh, bool balanced, bool append) {
-  return by_d<PA_BF16, PA_BF16>(d, gh, balanced, append);
+  return by_d<PA_BF16, PA_BF16, false>(d, gh, balanced, append);
 }
 
 }  // namespace pa

@@ -5,7 +5,7 @@
 namespace pa {
 
 KernelRef decode_kernels_f16_f16(int d, int gh, bool balanced, bool append) {
-  return by_d<PA_F16, PA_F16>(d, gh, balanced, append);
+  return by_d<PA_F16, PA_F16, false>(d, gh, balanced, append);
 }
 
 }  // namespace pa

@@ -1,0 +1,11 @@
+// Decode kernels for float16 queries and float16 caches, cache blocks of 32 to 256 tokens.
+
+#include "pa_decode_kernel.h"
+
+namespace pa {
+
+KernelRef decode_kernels_f16_f16_large(int d, int gh, bool balanced, bool append) {
+  return by_d<PA_F16, PA_F16, true>(d, gh, balanced, append);
+}
+
+}  // namespace pa

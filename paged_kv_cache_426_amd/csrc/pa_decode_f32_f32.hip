@@ -5,7 +5,7 @@
 namespace pa {
 
 KernelRef decode_kernels_f32_f32(int d, int gh, bool balanced, bool append) {
-  return by_d<PA_F32, PA_F32>(d, gh, balanced, append);
+  return by_d<PA_F32, PA_F32, false>(d, gh, balanced, append);
 }
 
 }  // namespace pa

@@ -5,9 +5,15 @@
 // What is computed: for each sequence b and query head h, one query row
 // attends over the sequence's n cached tokens, softmax(q K^T * scale) V
 // ("KV-Cache evolution" §1, attention formula), where token j's K/V row sits
-// in physical block block_tables[b][j / 16] at offset j % 16 ("PagedAttention
+// in physical block block_tables[b][j / bs] at offset j % bs ("PagedAttention
 // deep dive" §2.1; "vLLM inference principles", block-table figure), and
 // query head h reads KV head h / group ("KV-Cache evolution" §3A, GQA).
+//
+// Block size. The kernels work in 16-token sub-blocks. A cache of blocks of
+// bs = 16 * 2^k tokens, [NB, bs, Hkv, d], is byte for byte a pool of NB * 2^k
+// sub-blocks [NB * 2^k, 16, Hkv, d]: sub-block j of a sequence is sub-block
+// (block_tables[b][j >> k] << k) + (j & (2^k - 1)) of that pool. Everything
+// below ("block", "blocks per partition", ids) counts sub-blocks.
 //
 // Work decomposition. A workgroup (2 to 8 waves) serves one KV head and a run of
 // GH of its query heads, over a range of that KV head's cache blocks: a whole
@@ -83,9 +89,10 @@ struct DecodeParams {
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
-  int max_blocks_per_seq;
-  int mode;              // kSplitSingle / kSplitFixed / kSplitBalanced
-  int partition_blocks;  // fixed / single: blocks per partition
+  int max_blocks_per_seq;  // block-table row stride (physical blocks)
+  int sub_log2;            // log2(block_size / 16)
+  int mode;              // a SplitMode
+  int partition_blocks;  // fixed / single: sub-blocks per partition
   int max_partitions;    // stride of the partial arrays (see DecodeLaunch)
   int num_splits;        // balanced: number of shares S
   int direct;            // a range that is a whole sequence writes `out` directly
@@ -139,6 +146,9 @@ struct Geo {
   static constexpr int krs = row + 16;              // LDS row stride of the K tile
   static_assert(nkl >= 1 && nvl >= 1 && rvk * nkl == kBs, "unsupported geometry");
 };
+
+// 16-token sub-blocks holding n tokens
+__device__ __forceinline__ int num_blocks_of(int n) { return n > 0 ? (n + kBs - 1) / kBs : 0; }
 
 template <int QT> struct QOpT { using type = u32x4; };  // 8 x 16-bit
 template <> struct QOpT<PA_F32> { using type = float; };
@@ -310,9 +320,10 @@ struct AppendRow {
   static constexpr int vsrc = 8 * qb;           // source bytes per V piece
   u32x4 k;  // lane i < klanes: source elements of cache bytes [kcache i, kcache (i + 1))
   u32x4 v[vsrc / 16];
-  int blk;  // block (within the sequence) holding the new token; -1: none here
-  int t;    // its row in that block
-  int id;   // that block's physical id
+  int blk;  // sub-block (within the sequence) holding the new token; -1: none here
+  int t;    // its row in that sub-block
+  int id;   // the physical block's id (block-table entry)
+  int sub;  // the sub-block within that physical block
 };
 
 // The same row in cache encoding: lane i < klanes holds cache bytes
@@ -402,6 +413,12 @@ struct Item {
   int share, lo, hi;
 };
 
+// Block ids of a segment's units, one per lane (see fetch_ids).
+struct Ids {
+  int entry;  // block-table entry
+  int sub;    // 16-token sub-block within that block
+};
+
 struct Seg {
   int item;   // work item of the range
   int h0, g;  // its query heads and KV head
@@ -424,7 +441,7 @@ struct Seg {
 // first unit of the next segment is already being loaded (its block ids and
 // query fragments were fetched one segment ahead), so a switch between
 // ranges costs only the epilogue of the finished range.
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP>
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB>
 __device__ __forceinline__ void run_ranges(const DecodeParams &p,
                                            Shared<QT, KT, D, GH, NBI, NW> &sh, const Item (&items)[2],
                                            int n_items, int b_first, int n_first, int blo_first,
@@ -510,13 +527,18 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     if (sg.item != 0 || n_items < 2) return nx;
     return range_seg(1, items[1], uniform(sh.first[1]), u0);
   };
-  // lane i: physical id of block i % NBI of the segment's unit i / NBI
+  // lane i: block i % NBI of the segment's unit i / NBI -- the block-table
+  // entry of its physical block (loaded; used only where the unit's loads
+  // are issued, so that nothing waits for it earlier) and its sub-block
+  // within that physical block
   auto fetch_ids = [&](const Seg &sg) {
     const int kk = sg.c * kIdsUnits + lane / NBI;
     const int j = sg.blo + (sg.w0 + kk * NW) * NBI + lane % NBI;
     const bool ok = sg.valid && kk < sg.nk && j < sg.bhi;
     const int32_t *row = p.block_tables + (size_t)(sg.valid ? sg.b : 0) * p.max_blocks_per_seq;
-    return row[ok ? j : 0];
+    const int e = ok ? j : 0;
+    if constexpr (SUB) return Ids{row[e >> p.sub_log2], e & ((1 << p.sub_log2) - 1)};
+    else return Ids{row[e], 0};
   };
   // the appended token of sg's sequence, when sg's range holds it (loads
   // are issued in any case, of nothing otherwise)
@@ -540,7 +562,10 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     const __amdgpu_buffer_rsrc_t rt = block_rsrc(
         reinterpret_cast<const uint8_t *>(p.block_tables + (size_t)b * p.max_blocks_per_seq),
         here ? (uint32_t)p.max_blocks_per_seq * 4u : 0u);
-    a.id = (int)__builtin_amdgcn_raw_buffer_load_b32(rt, (uint32_t)lb * 4u, 0, 0);
+    // the physical block's id; its sub-block is added where it is used
+    const int lbe = SUB ? lb >> p.sub_log2 : lb;
+    a.id = (int)__builtin_amdgcn_raw_buffer_load_b32(rt, (uint32_t)lbe * 4u, 0, 0);
+    a.sub = SUB ? lb & ((1 << p.sub_log2) - 1) : 0;
     return a;
   };
   // query fragments (A operand) of sequence b: row tl holds head h0 + tl % GH
@@ -588,13 +613,15 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 
   // Loads of one unit of KV head g into a register stage: the unit whose
   // block ids start at lane u * NBI of `ids`; an invalid unit loads nothing.
-  auto issue = [&](int ids, int u, bool valid, int g, St &st) {
+  auto issue = [&](const Ids &ids, int u, bool valid, int g, St &st) {
     // head g's row 0 to the block end
     const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;
 #pragma unroll
     for (int bi = 0; bi < NBI; ++bi) {
       const int lidx = min(u * NBI + bi, kWave - 1);
-      const int id = __builtin_amdgcn_readlane(ids, lidx);
+      int id = __builtin_amdgcn_readlane(ids.entry, lidx);
+      if constexpr (SUB)  // the pool sub-block
+        id = (id << p.sub_log2) + __builtin_amdgcn_readlane(ids.sub, lidx);
       const size_t off = (size_t)id * blk_bytes + (size_t)g * G::row;
       const uint32_t n = valid ? blk_span : 0u;
       const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.k_cache + off, n);
@@ -799,7 +826,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   Seg cur = make_seg(0, items[0], b_first, n_first, blo_first, bhi_first, piece_first,
                      whole_first, 0, 0);
   // the first segment's loads go out before the LDS walk to the next one
-  int ids_cur = fetch_ids(cur);
+  Ids ids_cur = fetch_ids(cur);
   QOp q_cur[G::ksteps], q_nxt[G::ksteps];
   load_q(cur.b, items[0].h0, q_cur);
   // the appended row: loaded a segment ahead, encoded when its segment starts
@@ -807,8 +834,12 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   AE app{};
   // encoded only by a segment that holds it (the encoding divides)
   auto take_app = [&](const AR &a) {
-    if (a.blk >= 0) app = encode_append(a, p.k_scale, p.v_scale_w);
-    else app.blk = -1;
+    if (a.blk >= 0) {
+      app = encode_append(a, p.k_scale, p.v_scale_w);
+      if constexpr (SUB) app.id = (a.id << p.sub_log2) + a.sub;  // pool sub-block id
+    } else {
+      app.blk = -1;
+    }
   };
   if constexpr (APP) take_app(load_app(cur));
   Seg nxt = next_seg(cur);
@@ -816,7 +847,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   St st[NS];
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(ids_cur, s, s < cur.kn, cur.g, st[s]);
-  int ids_nxt = fetch_ids(nxt);
+  Ids ids_nxt = fetch_ids(nxt);
   load_q(nxt.valid ? nxt.b : cur.b, nxt.valid ? nxt.h0 : cur.h0, q_nxt);
   reset();
   for (;;) {
@@ -877,9 +908,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   }
 }
 
-__device__ __forceinline__ int num_blocks_of(int n) { return n > 0 ? (n + kBs - 1) / kBs : 0; }
-
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP>
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB>
 __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
   __shared__ Shared<QT, KT, D, GH, NBI, NW> sh;
   const int tid = threadIdx.x;
@@ -989,7 +1018,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
     first_piece = items[0].share + first_b;
     first_whole = first_lo == 0 && first_hi == en - st;
   }
-  run_ranges<QT, KT, D, GH, NBI, NS, NW, APP>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
+  run_ranges<QT, KT, D, GH, NBI, NS, NW, APP, SUB>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
                                      first_piece, first_whole);
 }
 
@@ -1017,53 +1046,62 @@ constexpr int balanced_waves() {
   return 8;
 }
 
-template <int QT, int KT, int D, int GH, bool APP>
+// SUB: blocks larger than 16 tokens (read as 16-token sub-blocks); the
+// 16-token kernels leave the sub-block arithmetic out.
+template <int QT, int KT, int D, int GH, bool APP, bool SUB>
 KernelRef kernel_of(bool balanced) {
   constexpr int NBI = units_of<QT, KT, GH>();
   constexpr int NWB = balanced_waves<QT, KT, D, GH, APP>();
   if (balanced)
-    return {reinterpret_cast<const void *>(&decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP>),
+    return {reinterpret_cast<const void *>(
+                &decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP, SUB>),
             NWB * kWave};
   return {reinterpret_cast<const void *>(
-              &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP>),
+              &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP, SUB>),
           kFixedWaves * kWave};
 }
 
-template <int QT, int KT, int D, int GH>
+template <int QT, int KT, int D, int GH, bool SUB>
 KernelRef with_append(bool balanced, bool append) {
-  return append ? kernel_of<QT, KT, D, GH, true>(balanced)
-                : kernel_of<QT, KT, D, GH, false>(balanced);
+  return append ? kernel_of<QT, KT, D, GH, true, SUB>(balanced)
+                : kernel_of<QT, KT, D, GH, false, SUB>(balanced);
 }
 
-template <int QT, int KT, int D>
+template <int QT, int KT, int D, bool SUB>
 KernelRef by_gh(int gh, bool balanced, bool append) {
   switch (gh) {
-    case 1: return with_append<QT, KT, D, 1>(balanced, append);
-    case 2: return with_append<QT, KT, D, 2>(balanced, append);
-    case 4: return with_append<QT, KT, D, 4>(balanced, append);
-    case 8: return with_append<QT, KT, D, 8>(balanced, append);
-    case 16: return with_append<QT, KT, D, 16>(balanced, append);
+    case 1: return with_append<QT, KT, D, 1, SUB>(balanced, append);
+    case 2: return with_append<QT, KT, D, 2, SUB>(balanced, append);
+    case 4: return with_append<QT, KT, D, 4, SUB>(balanced, append);
+    case 8: return with_append<QT, KT, D, 8, SUB>(balanced, append);
+    case 16: return with_append<QT, KT, D, 16, SUB>(balanced, append);
   }
   return {nullptr, 0};
 }
 
-template <int QT, int KT>
+template <int QT, int KT, bool SUB>
 KernelRef by_d(int d, int gh, bool balanced, bool append) {
   switch (d) {
-    case 64: return by_gh<QT, KT, 64>(gh, balanced, append);
-    case 128: return by_gh<QT, KT, 128>(gh, balanced, append);
+    case 64: return by_gh<QT, KT, 64, SUB>(gh, balanced, append);
+    case 128: return by_gh<QT, KT, 128, SUB>(gh, balanced, append);
   }
   return {nullptr, 0};
 }
 }  // namespace
 
-// The kernels of one element-type pair (one translation unit each): the
-// decode kernel for head size d, gh query heads per workgroup, the balanced
-// split or not, with append or not; {nullptr, 0} when not built.
+// The kernels of one element-type pair: the decode kernel for head size d,
+// gh query heads per workgroup, the balanced split or not, with append or
+// not; {nullptr, 0} when not built. Each pair has one translation unit for
+// 16-token blocks and one (_large) for larger blocks.
 KernelRef decode_kernels_f32_f32(int d, int gh, bool balanced, bool append);
 KernelRef decode_kernels_f16_f16(int d, int gh, bool balanced, bool append);
 KernelRef decode_kernels_bf16_bf16(int d, int gh, bool balanced, bool append);
 KernelRef decode_kernels_f16_fp8(int d, int gh, bool balanced, bool append);
 KernelRef decode_kernels_bf16_fp8(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_f32_f32_large(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_f16_f16_large(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_bf16_bf16_large(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_f16_fp8_large(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_bf16_fp8_large(int d, int gh, bool balanced, bool append);
 
 }  // namespace pa

@@ -85,6 +85,15 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mappin
 // fill every compute unit once at the decode kernel's occupancy.
 int balanced_num_splits(const DecodeLaunch &a);
 
+// Block sizes the decode kernels take: 16 << k tokens, k = 0 .. kMaxSubLog2
+// (16 to 256). Returns k, or -1 for any other size.
+constexpr int kMaxSubLog2 = 4;
+inline int sub_block_log2(int block_size) {
+  for (int k = 0; k <= kMaxSubLog2; ++k)
+    if (block_size == (16 << k)) return k;
+  return -1;
+}
+
 // heads of one KV group that one workgroup serves (a divisor of the group, <= 16)
 inline int heads_per_workgroup(int group) {
   return group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;

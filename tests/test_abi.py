@@ -77,7 +77,9 @@ def _decode(**kw):
     (dict(out=NULL), 1), (dict(q=NULL), 1), (dict(bt=NULL), 1),
     (dict(Hq=3), 2),                               # Hq % Hkv != 0
     (dict(B=-1), 2), (dict(Hkv=0), 2), (dict(NB=0), 2), (dict(MBS=0), 2),
-    (dict(d=96), 3), (dict(bs=32), 3),
+    (dict(d=96), 3), (dict(bs=8), 3), (dict(bs=48), 3), (dict(bs=512), 3),
+    (dict(bs=32, P=16), 2),                        # partition not a multiple of block_size
+    (dict(bs=256, NB=2 ** 28), 3),                 # 16-token sub-block ids exceed 32 bits
     (dict(qt=pa.PA_BF16, kt=pa.PA_F16), 3),        # mixed 16-bit types
     (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),  # fp8 cache needs a 16-bit query
     (dict(qt=7), 3),

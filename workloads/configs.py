@@ -135,10 +135,13 @@ def _slots_of_positions(block_table, positions, bs) -> np.ndarray:
 
 
 def _dense_workload(name, rng, ctx_lens, num_blocks, Hq, Hkv, d, bs, q_dtype, kv_dtype,
-                    partition_size, mbs=None) -> Workload:
-    """Pool filled with random values; one new token per sequence."""
+                    partition_size, mbs=None, contiguous=False) -> Workload:
+    """Pool filled with random values; one new token per sequence. Physical
+    blocks are handed out in a seeded random order, or in id order (each
+    sequence's blocks then sit next to each other) with ``contiguous``."""
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
-    pool = BlockPool(num_blocks, bs, order=rng.permutation(num_blocks))
+    order = np.arange(num_blocks) if contiguous else rng.permutation(num_blocks)
+    pool = BlockPool(num_blocks, bs, order=order)
     seqs, new_slots = _fill_then_append(pool, ctx_lens)
     mbs = mbs or max(-(-int(n) // bs) for n in ctx_lens)
     B = len(ctx_lens)
@@ -171,16 +174,25 @@ def tiny_fp32_gqa2(seed: int = 1, partition_size: int = 0) -> Workload:
                            "f32", "f32", partition_size)
 
 
-def llama3_8b_b32(seed: int = 2, partition_size: int = -1) -> Workload:
+def llama3_8b_b32(seed: int = 2, partition_size: int = -1, block_size: int = 16,
+                  placement: str = "permuted") -> Workload:
     """Llama-3-8B-shaped layer: batch 32, context lengths uniform on
     [512, 4096], 32 query / 8 KV heads, head_dim 128, bf16, block_size 16,
-    pool 10 % larger than the blocks in use, handed out in random order."""
+    pool 10 % larger than the blocks in use, handed out in random order.
+    ``block_size`` and ``placement`` ("permuted" or "contiguous") vary the
+    paging for the block-size study; the context lengths stay the same."""
+    if placement not in ("permuted", "contiguous"):
+        raise ValueError(f"placement {placement!r}")
     rng = np.random.default_rng(seed)
     ctx = rng.integers(512, 4096, size=32, endpoint=True)
-    needed = sum(-(-int(n) // 16) for n in ctx)
+    bs = int(block_size)
+    needed = sum(-(-int(n) // bs) for n in ctx)
     nb = math.ceil(1.1 * needed)
-    return _dense_workload("llama3_8b_b32", rng, ctx, nb, 32, 8, 128, 16,
-                           "bf16", "bf16", partition_size, mbs=4096 // 16)
+    name = "llama3_8b_b32" if (bs, placement) == (16, "permuted") else \
+        f"llama3_8b_b32_bs{bs}_{placement}"
+    return _dense_workload(name, rng, ctx, nb, 32, 8, 128, bs,
+                           "bf16", "bf16", partition_size, mbs=-(-4096 // bs),
+                           contiguous=placement == "contiguous")
 
 
 def mha_b32_ctx4096(seed: int = 3, partition_size: int = -1) -> Workload:
