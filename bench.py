@@ -67,6 +67,9 @@ def parse_args(argv=None):
     ap.add_argument("--fused-append", action="store_true",
                     help="one decode-with-append launch instead of the slot-write kernel "
                          "followed by decode (measured no faster on these workloads)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode through pa_decode_shared_prefix (workloads with groups of "
+                         "sequences sharing a prefix): shared blocks are read once per group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -294,6 +297,16 @@ def main(argv=None):
     # (decode_append), which needs every new token at its sequence's last
     # position.
     fused = new_s is not None and args.fused_append and new_token_is_last(wl)
+    shared = args.shared_prefix
+    if shared:
+        if wl.prefix_members is None:
+            print(f"--shared-prefix: workload {wl.name} has no prefix groups", file=sys.stderr)
+            return 2
+        gm = t(wl.prefix_members)
+        pl = t(wl.prefix_lens)
+        ws_sp = torch.empty(pa.decode_shared_prefix_workspace_size(
+            wl.num_seqs, gm.shape[0], gm.shape[1], wl.num_q_heads, wl.head_dim, wl.max_blocks_per_seq,
+            q.dtype), dtype=torch.uint8, device=dev)
 
     def step(i):
         kc, vc = layers[i % len(layers)]
@@ -306,6 +319,11 @@ def main(argv=None):
             return
         if new_s is not None:
             pa.reshape_and_cache(new_k, new_v, kc, vc, new_s, wl.k_scale, wl.v_scale)
+        if shared:
+            pa.decode_shared_prefix(q, kc, vc, bt, cl, gm, pl, scale=wl.scale,
+                                    k_scale=wl.k_scale, v_scale=wl.v_scale, out=out,
+                                    workspace=ws_sp)
+            return
         pa.decode(q, kc, vc, bt, cl, scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
                   partition_size=P, out=out, workspace=ws)
 
@@ -356,7 +374,13 @@ def main(argv=None):
         exp_sums = torch.empty((wl.num_q_heads, npc), dtype=torch.float32, device=dev)
         split_arg = -S
         log(f"balanced split: {S} shares")
-    if P:
+    if shared:
+        def kernel(i):
+            kc, vc = layers[i % len(layers)]
+            pa.decode_shared_prefix(q, kc, vc, bt, cl, gm, pl, scale=wl.scale,
+                                    k_scale=wl.k_scale, v_scale=wl.v_scale, out=out,
+                                    workspace=ws_sp)
+    elif P:
         def kernel(i):
             kc, vc = layers[i % len(layers)]
             pa.decode_partials(q, kc, vc, bt, cl, split_arg, scale=wl.scale, k_scale=wl.k_scale,
@@ -402,6 +426,11 @@ def main(argv=None):
     if not P:
         kernel_alg += db["out"]
     step_alg = db["total"] + (append_bytes(wl) if fused else write_bytes(wl)) + copy_bytes(wl)
+    if shared:
+        # every distinct K/V row once: shared blocks are read once per group
+        ub = unique_kv_bytes(wl)
+        kernel_alg = ub + db["q"] + db["out"] + db["tables"] + db["ctx_lens"]
+        step_alg += ub - db["kv"]
     tokens = wl.tokens_attended
     step_s = ms_per_step / 1e3
     achieved = kernel_alg / kern_avg_s / 1e9
@@ -438,7 +467,8 @@ def main(argv=None):
             "step": ("copy_blocks + " if has_cow else "") +
                     ("decode_append (new tokens' slot writes in the decode launch)" if fused
                      else "reshape_and_cache(new tokens) + decode") +
-                    (" (partials + merge)" if P else " (single pass)"),
+                    (" shared-prefix (prep + prefix pass + suffix pass + merge)" if shared
+                     else " (partials + merge)" if P else " (single pass)"),
         },
         "gbps": step_alg / step_s / 1e9,
         "hbm_frac": step_alg / step_s / 1e9 / HBM_PEAK_GBPS,
@@ -449,15 +479,18 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": committed_traffic(wl.name, P),
-            "kernel": "decode_kernel" + (" (split partials)" if P else " (single pass)") +
-                      ("; the step runs its variant with the slot write fused" if fused else ""),
+            "traffic": None if shared else committed_traffic(wl.name, P),
+            "kernel": ("shared-prefix decode: prep, prefix-pass and suffix-pass decode kernels "
+                       "and merge, timed together, against the distinct K/V bytes" if shared
+                       else "decode_kernel" + (" (split partials)" if P else " (single pass)") +
+                       ("; the step runs its variant with the slot write fused"
+                        if fused else "")),
             "kernel_avg_us": kern_avg_s * 1e6,
             "kernel_timing": f"HIP events around {n_launch} back-to-back launches",
             "kernel_bracketed_median_us": kern_med_s * 1e6,
             "algorithmic_bytes_per_launch": kernel_alg,
             "bytes_per_unit": db["kv_per_token"],
-            "units_per_launch": tokens,
+            "units_per_launch": (unique_kv_bytes(wl) // db["kv_per_token"]) if shared else tokens,
         },
     }
     if "distinct_blocks" in wl.info:

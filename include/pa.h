@@ -314,6 +314,62 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapp
                          int num_pairs, int num_kv_heads, int head_dim, int block_size,
                          int num_blocks, int cache_dtype, void *stream);
 
+/*
+ * pa_decode_shared_prefix -- decode for groups of sequences that share a
+ * prompt prefix, reading each shared block once per group.
+ *
+ * Sequences forked from one prompt (parallel sampling, beam search) hold the
+ * prompt's blocks by reference ("PagedAttention deep dive", section 2.3;
+ * "KV-cache sharing article", sections 3.1 and 4.2). Group g lists its
+ * member sequences in group_members[g, 0 .. group_size) (-1 marks an empty
+ * slot; every sequence is in at most one group) and its shared prefix length
+ * prefix_lens[g] in tokens. The result is the same attention as pa_decode
+ * for every sequence (up to floating-point rounding order):
+ *
+ *   out[b, h, :] = softmax(scale * q[b, h] . K_b^T) V_b over all context_lens[b]
+ *                  tokens of sequence b.
+ *
+ * It is computed in two passes of the balanced split: the prefix of each
+ * group, with the members' query rows stacked as extra query heads of each
+ * KV head (so a prefix block is read once for all members), and each
+ * sequence's suffix past its group's prefix; then the pieces of both passes
+ * are merged with their softmax statistics, as in pa_decode_reduce.
+ *
+ * Arguments as pa_decode (balanced split), plus
+ *   group_members  [num_groups, group_size] int32, device: sequence ids.
+ *   prefix_lens    [num_groups] int32, device: shared prefix tokens of each
+ *                  group. Only whole blocks count: the prefix used is
+ *                  floor(prefix_lens[g] / block_size) blocks (capped at
+ *                  max_blocks_per_seq); tokens past it are read per sequence.
+ *   workspace      device scratch of at least
+ *                  pa_decode_shared_prefix_workspace_size(...) bytes; its
+ *                  contents are ignored and overwritten.
+ *
+ * Preconditions (device data, unchecked): the first prefix blocks of every
+ * member's block table are the same physical blocks, and every member's
+ * context length is at least its group's prefix; a sequence appears in at
+ * most one slot. Sequences in no group are decoded over their whole context.
+ * num_seqs and num_groups at most 1024; q_dtype f32, f16 or bf16 (the output
+ * type).
+ *
+ * Errors: as pa_decode; PA_ERR_BAD_SHAPE for num_groups or group_size < 1;
+ * PA_ERR_NULL_POINTER without group_members, prefix_lens or workspace;
+ * PA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int group_size,
+                                              int num_q_heads, int head_dim,
+                                              int max_blocks_per_seq, int q_dtype);
+
+pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, const int32_t *group_members,
+                                  const int32_t *prefix_lens, int num_seqs, int num_groups,
+                                  int group_size, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks,
+                                  int max_blocks_per_seq, float scale, int q_dtype,
+                                  int kv_dtype, float k_scale, float v_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN",
     "PaError", "lib", "library_path", "dtype_code",
-    "decode", "decode_partials", "decode_reduce", "decode_workspace_size",
+    "decode", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
+    "decode_shared_prefix", "decode_shared_prefix_workspace_size",
     "num_partitions", "decode_balanced_splits", "reshape_and_cache", "copy_blocks",
     "PARTITION_AUTO",
 ]
@@ -85,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 7 + [f32, f32, vp]
         L.pa_copy_blocks.restype = i32
         L.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
+        L.pa_decode_shared_prefix_workspace_size.restype = sz
+        L.pa_decode_shared_prefix_workspace_size.argtypes = [i32] * 7
+        L.pa_decode_shared_prefix.restype = i32
+        L.pa_decode_shared_prefix.argtypes = ([vp] * 8 + [i32] * 9 +
+                                              [f32, i32, i32, f32, f32, vp, sz, vp])
         _LIB = L
     return _LIB
 
@@ -188,6 +194,51 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            _ptr(context_lens), B, Hq, Hkv, d, bs, NB, MBS, float(scale),
                            dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
                            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def decode_shared_prefix_workspace_size(num_seqs: int, num_groups: int, group_size: int,
+                                        num_q_heads: int, head_dim: int,
+                                        max_blocks_per_seq: int, q_dtype: torch.dtype) -> int:
+    return lib().pa_decode_shared_prefix_workspace_size(
+        num_seqs, num_groups, group_size, num_q_heads, head_dim, max_blocks_per_seq,
+        _DTYPES[q_dtype])
+
+
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         group_members: torch.Tensor, prefix_lens: torch.Tensor,
+                         scale: Optional[float] = None, k_scale: float = 1.0,
+                         v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode for groups of sequences sharing a prompt prefix, each shared
+    block read once per group (C: pa_decode_shared_prefix). group_members
+    [G, M] int32 (sequence ids, -1 for an empty slot), prefix_lens [G] int32
+    (tokens). Returns out [B, Hq, d] in q's type: the same attention as
+    decode()."""
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, group_members, prefix_lens, out,
+               workspace)
+    B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if group_members.dim() != 2 or prefix_lens.shape != (group_members.shape[0],):
+        raise PaError("group_members must be [G, M] and prefix_lens [G]")
+    _i32(group_members, "group_members")
+    _i32(prefix_lens, "prefix_lens")
+    G, M = group_members.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PaError("out must match q in shape and type")
+    if workspace is None:
+        need = decode_shared_prefix_workspace_size(B, G, M, Hq, d, MBS, q.dtype)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(group_members), _ptr(prefix_lens), B, G, M, Hq, Hkv, d, bs, NB, MBS, float(scale),
+        dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale), _ptr(workspace),
+        ws_bytes, _stream(dev)))
     return out
 
 

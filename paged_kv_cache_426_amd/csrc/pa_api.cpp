@@ -360,4 +360,136 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapp
                                           stream));
 }
 
+
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of a shared-prefix decode: q_stack, the prefix and suffix tables
+// and lengths, the sequence slots, then both passes' partials; each part
+// 256-byte aligned. Fills *ws when base is non-null; returns the total.
+size_t shared_prefix_layout(char *base, int B, int G, int M, int Hq, int d, int mbs, int q_bytes,
+                            int a_splits, int b_splits, pa::SharedPrefixWorkspace *ws) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const size_t a_pieces = (size_t)Hq * M * ((size_t)a_splits + G);
+  const size_t b_pieces = (size_t)Hq * ((size_t)b_splits + B);
+  char *q_stack = take((size_t)G * Hq * M * d * q_bytes);
+  char *prefix_tables = take((size_t)G * mbs * 4);
+  char *prefix_ctx = take((size_t)G * 4);
+  char *suffix_tables = take((size_t)B * mbs * 4);
+  char *suffix_lens = take((size_t)B * 4);
+  char *seq_slot = take((size_t)B * 4);
+  char *a_out = take(a_pieces * d * 4);
+  char *a_max = take(a_pieces * 4);
+  char *a_sum = take(a_pieces * 4);
+  char *b_out = take(b_pieces * d * 4);
+  char *b_max = take(b_pieces * 4);
+  char *b_sum = take(b_pieces * 4);
+  if (ws) {
+    ws->q_stack = q_stack;
+    ws->prefix_tables = reinterpret_cast<int32_t *>(prefix_tables);
+    ws->prefix_ctx = reinterpret_cast<int32_t *>(prefix_ctx);
+    ws->suffix_tables = reinterpret_cast<int32_t *>(suffix_tables);
+    ws->suffix_lens = reinterpret_cast<int32_t *>(suffix_lens);
+    ws->seq_slot = reinterpret_cast<int32_t *>(seq_slot);
+    ws->a_out = reinterpret_cast<float *>(a_out);
+    ws->a_max = reinterpret_cast<float *>(a_max);
+    ws->a_sum = reinterpret_cast<float *>(a_sum);
+    ws->b_out = reinterpret_cast<float *>(b_out);
+    ws->b_max = reinterpret_cast<float *>(b_max);
+    ws->b_sum = reinterpret_cast<float *>(b_sum);
+  }
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int group_size,
+                                              int num_q_heads, int head_dim,
+                                              int max_blocks_per_seq, int q_dtype) {
+  if (num_seqs <= 0 || num_groups <= 0 || group_size <= 0 || num_q_heads <= 0 ||
+      head_dim <= 0 || max_blocks_per_seq <= 0 || !known_dtype(q_dtype) ||
+      q_dtype == PA_FP8_E4M3FN)
+    return 0;
+  return shared_prefix_layout(nullptr, num_seqs, num_groups, group_size, num_q_heads, head_dim,
+                              max_blocks_per_seq, elem_bytes(q_dtype), pa::kMaxAutoSplits,
+                              pa::kMaxAutoSplits, nullptr);
+}
+
+pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, const int32_t *group_members,
+                                  const int32_t *prefix_lens, int num_seqs, int num_groups,
+                                  int group_size, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks,
+                                  int max_blocks_per_seq, float scale, int q_dtype,
+                                  int kv_dtype, float k_scale, float v_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  if (!out || !group_members || !prefix_lens) return PA_ERR_NULL_POINTER;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                              max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale, -1);
+  if (st != PA_OK) return st;
+  if (num_groups <= 0 || group_size <= 0) return PA_ERR_BAD_SHAPE;
+  if (num_groups > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  // the prefix pass has group_size times the query heads
+  const long long hq_stacked = (long long)num_q_heads * group_size;
+  if (hq_stacked > INT_MAX / 2 || (long long)num_groups * group_size > INT_MAX / 2)
+    return PA_ERR_UNSUPPORTED;
+  const int gs = (int)(hq_stacked / num_kv_heads);
+  if ((long long)num_kv_heads * (gs / pa::heads_per_workgroup(gs)) > 65535)
+    return PA_ERR_UNSUPPORTED;
+  if (!workspace) return PA_ERR_NULL_POINTER;
+  if (num_seqs == 0) return PA_OK;
+  pa::SharedPrefixLaunch a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.group_members = group_members;
+  a.prefix_lens = prefix_lens;
+  a.num_seqs = num_seqs;
+  a.num_groups = num_groups;
+  a.group_size = group_size;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  a.q_elem_bytes = elem_bytes(q_dtype);
+  pa::DecodeLaunch probe{};
+  probe.q_dtype = q_dtype;
+  probe.kv_dtype = kv_dtype;
+  probe.head_dim = head_dim;
+  probe.num_kv_heads = num_kv_heads;
+  probe.num_q_heads = (int)hq_stacked;
+  a.prefix_splits = pa::balanced_num_splits(probe);
+  probe.num_q_heads = num_q_heads;
+  a.suffix_splits = pa::balanced_num_splits(probe);
+  const size_t need = shared_prefix_layout(nullptr, num_seqs, num_groups, group_size, num_q_heads,
+                                           head_dim, max_blocks_per_seq, a.q_elem_bytes,
+                                           a.prefix_splits, a.suffix_splits, nullptr);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  shared_prefix_layout(static_cast<char *>(workspace), num_seqs, num_groups, group_size,
+                       num_q_heads, head_dim, max_blocks_per_seq, a.q_elem_bytes,
+                       a.prefix_splits, a.suffix_splits, &a.ws);
+  return status_of(pa::launch_shared_prefix(a, stream));
+}
+
 }  // extern "C"

@@ -81,6 +81,35 @@ int launch_reshape_and_cache(const void *key, const void *value, void *k_cache, 
 int launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
                        int num_pairs, size_t block_bytes, void *stream);
 
+// Device scratch of a shared-prefix decode, carved from the caller's workspace.
+struct SharedPrefixWorkspace {
+  void *q_stack;            // [G, Hq * M, d], q's type
+  int32_t *prefix_tables;   // [G, MBS]
+  int32_t *prefix_ctx;      // [G]
+  int32_t *suffix_tables;   // [B, MBS]
+  int32_t *suffix_lens;     // [B]
+  int32_t *seq_slot;        // [B]
+  float *a_out, *a_max, *a_sum;  // prefix pass partials, balanced layout
+  float *b_out, *b_max, *b_sum;  // suffix pass partials, balanced layout
+};
+
+struct SharedPrefixLaunch {
+  void *out;
+  const void *q, *k_cache, *v_cache;
+  const int32_t *block_tables, *context_lens;
+  const int32_t *group_members;  // [G, M] sequence ids (-1: empty slot)
+  const int32_t *prefix_lens;    // [G] shared prefix tokens
+  int num_seqs, num_groups, group_size;
+  int num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
+  float scale, k_scale, v_scale;
+  int q_dtype, kv_dtype, q_elem_bytes;
+  int prefix_splits, suffix_splits;  // balanced-split shares of the two passes
+  SharedPrefixWorkspace ws;
+};
+
+// Prep, prefix pass, suffix pass and merge, in stream order.
+int launch_shared_prefix(const SharedPrefixLaunch &a, void *stream);
+
 // Shares a balanced split uses on the current device: enough workgroups to
 // fill every compute unit once at the decode kernel's occupancy.
 int balanced_num_splits(const DecodeLaunch &a);

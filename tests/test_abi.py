@@ -170,6 +170,41 @@ def test_reshape_and_copy_validation():
     assert cb(FAKE, FAKE, FAKE, 0, 2, 64, 16, 4, pa.PA_F32, NULL) == 0
 
 
+def _shared(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, gm=FAKE, pl=FAKE, B=8, G=2,
+                M=4, Hq=32, Hkv=8, d=128, bs=16, NB=64, MBS=8, scale=0.0884, qt=pa.PA_BF16,
+                kt=pa.PA_BF16, ks=1.0, vs=1.0, ws=FAKE, wsb=10, stream=NULL)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_decode_shared_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["gm"], a["pl"], a["B"], a["G"],
+        a["M"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["NB"], a["MBS"], a["scale"], a["qt"],
+        a["kt"], a["ks"], a["vs"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gm=NULL), 1), (dict(pl=NULL), 1), (dict(out=NULL), 1), (dict(ws=NULL), 1),
+    (dict(G=0), 2), (dict(M=0), 2), (dict(Hq=30), 2),
+    (dict(G=1025), 3), (dict(B=1025), 3), (dict(d=96), 3), (dict(bs=8), 3),
+    (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),
+    (dict(Hq=65536 * 8, Hkv=65536), 3),            # stacked heads: launch grid limit
+    (dict(), 4),                                   # workspace too small
+    (dict(B=0), 0),                                # no sequences: no-op
+])
+def test_decode_shared_prefix_validation(kw, status):
+    assert _shared(**kw) == status
+
+
+def test_shared_prefix_workspace_size():
+    f = pa.lib().pa_decode_shared_prefix_workspace_size
+    assert f(0, 2, 4, 32, 128, 8, pa.PA_BF16) == 0
+    assert f(8, 2, 4, 32, 128, 8, pa.PA_FP8_E4M3FN) == 0   # q is never fp8
+    n = f(64, 16, 4, 32, 128, 137, pa.PA_BF16)
+    # at least both passes' partials at the largest automatic share count
+    assert n >= (32 * 4 * (2048 + 16) + 32 * (2048 + 64)) * 130 * 4
+    assert n % 256 == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 

@@ -81,3 +81,26 @@ def test_permute_keeps_logical_content():
     bs = wl.block_size
     for s_old, s_new in zip(wl.new_slots, wp.new_slots):
         assert np.array_equal(wl.k_cache.reshape(-1, 2, 16)[s_old], wp.k_cache.reshape(-1, 2, 16)[s_new])
+
+
+def test_shared_prefix_lens_of_forked_groups():
+    """Groups of forked samples share every whole prompt block: 2048 prompt
+    tokens (the 8 tokens the parent decoded sit in a block that three of the
+    four samples copied before writing)."""
+    wl = W.build("shared_prefix_cow_b64")
+    assert wl.prefix_members.shape == (16, 4)
+    assert (wl.prefix_lens == 2048).all()
+
+
+def test_shared_prefix_lens_small_cases():
+    bt = np.array([[5, 6, 7, 8],
+                   [5, 6, 9, 10],
+                   [5, 6, 7, 11],
+                   [1, 2, 3, 4]], dtype=np.int32)
+    ctx = np.array([60, 64, 33, 64], dtype=np.int32)
+    members = np.array([[0, 1, -1], [0, 2, -1], [3, -1, -1], [-1, -1, -1]], dtype=np.int32)
+    got = W.shared_prefix_lens(bt, ctx, 16, members)
+    # {0, 1}: two common blocks; {0, 2}: three common, but sequence 2 holds
+    # only two whole blocks (33 tokens); {3}: all four of its whole blocks;
+    # no members: 0
+    assert got.tolist() == [32, 32, 64, 0]

@@ -16,6 +16,7 @@ from .configs import (
     long_ctx_fp8_b8,
     mha_b32_ctx4096,
     shared_prefix_cow_b64,
+    shared_prefix_lens,
     tiny_fp32_gqa2,
     permute_physical,
     unshare,
@@ -34,6 +35,7 @@ __all__ = [
     "long_ctx_fp8_b8",
     "mha_b32_ctx4096",
     "shared_prefix_cow_b64",
+    "shared_prefix_lens",
     "tiny_fp32_gqa2",
     "permute_physical",
     "unshare",

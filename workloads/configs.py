@@ -79,6 +79,11 @@ class Workload:
     new_slots: Optional[np.ndarray] = None    # [B] int64
     partition_size: int = 0                   # launch configuration: 0 single pass, >0 tokens
                                               # per partition, <0 balanced split (-1: automatic)
+    # groups of sequences sharing a prompt prefix: member ids [G, M] (-1 for
+    # an empty slot) and the shared prefix in tokens [G]; None when no
+    # sequences share blocks
+    prefix_members: Optional[np.ndarray] = None
+    prefix_lens: Optional[np.ndarray] = None
     info: Dict = field(default_factory=dict)
 
     @property
@@ -127,6 +132,25 @@ def _fill_then_append(pool: BlockPool, ctx_lens) -> (List, np.ndarray):
         seqs.append(s)
         new_slots.append(slot)
     return seqs, np.asarray(new_slots, dtype=np.int64)
+
+
+def shared_prefix_lens(block_tables, context_lens, block_size, members) -> np.ndarray:
+    """Shared prefix of each group, in tokens: the leading whole blocks that
+    every member's block table holds alike (the blocks a fork shares by
+    reference), no further than any member's context reaches with whole
+    blocks. members [G, M], -1 for an empty slot."""
+    out = np.zeros(len(members), dtype=np.int32)
+    for g, row in enumerate(members):
+        ids = [int(b) for b in row if b >= 0]
+        if not ids:
+            continue
+        k = min(int(context_lens[b]) // block_size for b in ids)
+        first = block_tables[ids[0]]
+        j = 0
+        while j < k and all(block_tables[b][j] == first[j] for b in ids[1:]):
+            j += 1
+        out[g] = j * block_size
+    return out
 
 
 def _slots_of_positions(block_table, positions, bs) -> np.ndarray:
@@ -261,16 +285,19 @@ def shared_prefix_cow_b64(seed: int = 4, partition_size: int = -1, groups: int =
     new_key = normal(rng, (B, Hkv, d), "bf16")
     new_value = normal(rng, (B, Hkv, d), "bf16")
     distinct_blocks = len({blk for s in seqs for blk in s.block_table})
+    members = np.arange(B, dtype=np.int32).reshape(groups, samples)
+    tables = _tables(seqs, mbs)
     return Workload(
         name="shared_prefix_cow_b64", num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv,
         head_dim=d, block_size=bs, num_blocks=nb, q_dtype="bf16", kv_dtype="bf16",
-        q=q, k_cache=k_cache, v_cache=v_cache, block_tables=_tables(seqs, mbs),
+        q=q, k_cache=k_cache, v_cache=v_cache, block_tables=tables,
         context_lens=ctx, scale=float(np.float32(1.0 / math.sqrt(d))),
         cow_pairs=np.asarray(cow, dtype=np.int64).reshape(-1, 2),
         hist_key=hist_key, hist_value=hist_value,
         hist_slots=np.asarray(hist, dtype=np.int64), hist_seq=np.asarray(owner, dtype=np.int32),
         new_key=new_key, new_value=new_value, new_slots=np.asarray(new, dtype=np.int64),
-        partition_size=partition_size,
+        partition_size=partition_size, prefix_members=members,
+        prefix_lens=shared_prefix_lens(tables, ctx, bs, members),
         info={"blocks_used": pool.blocks_in_use(), "shared_ratio": pool.shared_ratio(),
               "shared_ratio_after_fork": ratio_fork, "distinct_blocks": distinct_blocks,
               "groups": groups, "samples": samples},
