@@ -14,7 +14,8 @@ Array conventions (the stored element type is carried by the numpy dtype):
 * ``float32``  -- IEEE binary32 values;
 * ``float16``  -- IEEE binary16 values;
 * ``uint16``   -- bfloat16 bit patterns;
-* ``uint8``    -- OCP E4M3FN (fp8) codes.
+* ``uint8``    -- OCP E4M3FN (fp8) codes;
+* ``int8``     -- symmetric int8 codes (value = code x the tensor's scale).
 
 Sources, cited by page title and section (all four pages are about the KV
 cache and PagedAttention):
@@ -37,6 +38,8 @@ from .numerics import (
     bf16_bits_to_f64,
     e4m3fn_decode,
     e4m3fn_encode,
+    int8_decode,
+    int8_encode,
     to_f64,
 )
 from .attention import (
@@ -55,6 +58,8 @@ __all__ = [
     "bf16_bits_to_f64",
     "e4m3fn_decode",
     "e4m3fn_encode",
+    "int8_decode",
+    "int8_encode",
     "to_f64",
     "paged_decode",
     "paged_decode_partials",

@@ -54,7 +54,7 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
 
     ``scale`` is the softmax scale (normally 1/sqrt(d)), taken as the float32
     value the caller passes and widened exactly. ``k_scale`` / ``v_scale``
-    multiply the widened cache values (per-tensor dequantisation of an fp8
+    multiply the widened cache values (per-tensor dequantisation of an 8-bit
     cache; 1.0 otherwise). A sequence with context length 0 attends over
     nothing; its output is defined as zeros.
 

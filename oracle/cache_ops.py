@@ -21,20 +21,21 @@ Stored element conventions are those of ``oracle.numerics``.
 
 import numpy as np
 
-from .numerics import e4m3fn_encode, to_f32_exact
+from .numerics import e4m3fn_encode, int8_encode, to_f32_exact
 
 
 def _encode_rows(rows: np.ndarray, cache_dtype, scale) -> np.ndarray:
     """Bit copy when the source and cache element types match; otherwise the
-    fp8 quantisation e4m3fn(float32(x) / float32(scale)) with a correctly
-    rounded float32 division (numpy's float32 divide is IEEE)."""
+    8-bit quantisation e4m3fn(float32(x) / float32(scale)) (fp8 cache) or
+    int8(float32(x) / float32(scale)) (int8 cache) with a correctly rounded
+    float32 division (numpy's float32 divide is IEEE)."""
     if rows.dtype == cache_dtype:
         return rows.copy()
-    if cache_dtype == np.uint8:
+    if cache_dtype in (np.uint8, np.int8):
         x32 = to_f32_exact(rows)
         q = x32 / np.float32(scale)
         assert q.dtype == np.float32
-        return e4m3fn_encode(q)
+        return e4m3fn_encode(q) if cache_dtype == np.uint8 else int8_encode(q)
     raise TypeError(f"unsupported slot write {rows.dtype} -> {cache_dtype}")
 
 

@@ -86,11 +86,34 @@ def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
     return out
 
 
+INT8_MAX = 127
+
+
+def int8_encode(x: np.ndarray) -> np.ndarray:
+    """float32 values -> symmetric int8 codes: round to nearest, ties to even,
+    saturating to [-127, 127]; NaN -> 0.
+
+    The pages name INT8 KV storage beside FP8 ("PagedAttention deep dive" §4;
+    "KV-Cache evolution" §3C) without a scheme. The reading taken: symmetric
+    codes, the value of code c being c times the tensor's scale, -128 never
+    produced (so negation is exact).
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    q = np.clip(np.rint(np.where(nan, 0.0, x)), -INT8_MAX, INT8_MAX)
+    return q.astype(np.int8)
+
+
+def int8_decode(codes: np.ndarray) -> np.ndarray:
+    """int8 codes -> float64 (exact): the code itself, to be scaled."""
+    return np.asarray(codes, dtype=np.int8).astype(np.float64)
+
+
 def to_f64(a: np.ndarray) -> np.ndarray:
     """Widen a stored array to float64 using the dtype convention of the package.
 
     float32 / float16 widen exactly through numpy; uint16 is bfloat16 bits;
-    uint8 is E4M3FN codes.
+    uint8 is E4M3FN codes; int8 is symmetric int8 codes.
     """
     a = np.asarray(a)
     if a.dtype == np.float64:
@@ -101,6 +124,8 @@ def to_f64(a: np.ndarray) -> np.ndarray:
         return bf16_bits_to_f64(a)
     if a.dtype == np.uint8:
         return e4m3fn_decode(a)
+    if a.dtype == np.int8:
+        return int8_decode(a)
     raise TypeError(f"no stored-element convention for numpy dtype {a.dtype}")
 
 
