@@ -40,8 +40,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
 DEFAULT_WORKLOAD = "llama3_8b_b32"
-DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn"}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1}
+DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn",
+              "int8": "int8"}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1, "int8": 1}
 # the decode kernel's sources (the traffic counters are tied to them)
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_426_amd", "csrc", f)
                for f in ("pa_decode_kernel.h", "pa_device.h")]

@@ -48,8 +48,9 @@
  * sharing article" sections 2 and 4), any block size for the slot write and
  * the block copy; any num_q_heads that is a multiple of num_kv_heads; (q, kv)
  * element types (f32, f32), (f16, f16), (bf16, bf16), (f16, fp8_e4m3fn),
- * (bf16, fp8_e4m3fn). Decode reads a block of 16 * 2^k tokens as 2^k
- * consecutive 16-token sub-blocks.
+ * (bf16, fp8_e4m3fn), (f16, int8), (bf16, int8) (int8 caches: decode with
+ * block_size 16). Decode reads a block of 16 * 2^k tokens as 2^k consecutive
+ * 16-token sub-blocks.
  */
 #ifndef PA_H
 #define PA_H
@@ -71,12 +72,17 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = 5             /* the HIP runtime refused a kernel launch            */
 } pa_status;
 
-/* Element types. fp8_e4m3fn is OCP E4M3FN (bias 7, max 448, no infinities). */
+/* Element types. fp8_e4m3fn is OCP E4M3FN (bias 7, max 448, no infinities).
+ * int8 is a symmetric int8 code c in [-127, 127] standing for c * scale (the
+ * pages name INT8 and FP8 KV quantisation: "PagedAttention deep dive",
+ * section 4; "KV-Cache evolution", section 3C). Both 8-bit types are cache
+ * types only, with one fp32 scale per tensor (k_scale, v_scale). */
 typedef enum pa_dtype {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
-  PA_FP8_E4M3FN = 3
+  PA_FP8_E4M3FN = 3,
+  PA_INT8 = 4
 } pa_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -153,7 +159,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  * inference principles", block-table figure); fp8 storage of the cache
  * ("PagedAttention deep dive", sections 3.2 and 4; "KV-Cache evolution",
  * section 3C) with per-tensor scales k_scale / v_scale (ignored unless
- * kv_dtype is PA_FP8_E4M3FN).
+ * kv_dtype is PA_FP8_E4M3FN or PA_INT8: an 8-bit code then stands for its
+ * value times the scale).
  *
  *   out           [num_seqs, num_q_heads, head_dim], q_dtype; must not alias
  *                 any input.
@@ -287,7 +294,11 @@ pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_log
  *   key, value    [num_tokens, num_kv_heads, head_dim], src_dtype (f32, f16,
  *                 bf16)
  *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim],
- *                 cache_dtype == src_dtype, or PA_FP8_E4M3FN from f16/bf16/f32
+ *                 cache_dtype == src_dtype, or PA_FP8_E4M3FN / PA_INT8 from
+ *                 f16/bf16/f32: fp8 e4m3fn(x / scale) rounded to nearest even
+ *                 and saturated to +-448, or int8 rint(x / scale) (ties to
+ *                 even) saturated to [-127, 127] (NaN -> 0), the division in
+ *                 IEEE float32
  *   slot_mapping  [num_tokens] int64, slots distinct among non-negative entries
  * num_tokens == 0 is a no-op (key, value and slot_mapping may then be NULL).
  */

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN",
+    "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN", "PA_INT8",
     "PaError", "lib", "library_path", "dtype_code",
     "decode", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
     "decode_shared_prefix", "decode_shared_prefix_workspace_size",
@@ -28,7 +28,7 @@ __all__ = [
 # partition_size of the balanced split with the automatic share count
 PARTITION_AUTO = -1
 
-PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3FN, PA_INT8 = 0, 1, 2, 3, 4
 
 _DTYPES = {
     torch.float32: PA_F32,
@@ -36,6 +36,7 @@ _DTYPES = {
     torch.bfloat16: PA_BF16,
     torch.float8_e4m3fn: PA_FP8_E4M3FN,
     torch.uint8: PA_FP8_E4M3FN,  # raw E4M3FN codes
+    torch.int8: PA_INT8,         # symmetric int8 codes
 }
 _TORCH_OF = {PA_F32: torch.float32, PA_F16: torch.float16, PA_BF16: torch.bfloat16}
 

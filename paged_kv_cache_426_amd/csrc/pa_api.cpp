@@ -13,14 +13,17 @@ namespace {
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 bool known_dtype(int t) {
-  return t == PA_F32 || t == PA_F16 || t == PA_BF16 || t == PA_FP8_E4M3FN;
+  return t == PA_F32 || t == PA_F16 || t == PA_BF16 || t == PA_FP8_E4M3FN || t == PA_INT8;
 }
 
-int elem_bytes(int t) { return t == PA_F32 ? 4 : t == PA_FP8_E4M3FN ? 1 : 2; }
+int elem_bytes(int t) { return t == PA_F32 ? 4 : (t == PA_FP8_E4M3FN || t == PA_INT8) ? 1 : 2; }
+
+// 8-bit cache types: codes scaled by k_scale / v_scale
+bool quantised(int t) { return t == PA_FP8_E4M3FN || t == PA_INT8; }
 
 bool supported_decode_pair(int q, int kv) {
   if (q == kv) return q == PA_F32 || q == PA_F16 || q == PA_BF16;
-  return kv == PA_FP8_E4M3FN && (q == PA_F16 || q == PA_BF16);
+  return quantised(kv) && (q == PA_F16 || q == PA_BF16);
 }
 
 pa_status status_of(int hip_err) { return hip_err == 0 ? PA_OK : PA_ERR_LAUNCH; }
@@ -43,8 +46,10 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
   if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
   if (partition_size < 0 && num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return PA_ERR_BAD_SHAPE;
-  if (kv_dtype == PA_FP8_E4M3FN && (!isfinite(k_scale) || !isfinite(v_scale)))
+  if (quantised(kv_dtype) && (!isfinite(k_scale) || !isfinite(v_scale)))
     return PA_ERR_BAD_SHAPE;
+  // int8 decode kernels are built for 16-token blocks only
+  if (kv_dtype == PA_INT8 && block_size != 16) return PA_ERR_UNSUPPORTED;
   // launch-grid and in-kernel 32-bit offset limits
   const long long row_bytes = (long long)num_kv_heads * head_dim * elem_bytes(kv_dtype);
   if (row_bytes * block_size >= INT_MAX) return PA_ERR_UNSUPPORTED;
@@ -310,7 +315,7 @@ pa_status pa_decode_append(void *out, const void *q, const void *key, const void
                            size_t workspace_bytes, void *stream) {
   if (!key || !value) return PA_ERR_NULL_POINTER;
   // the new token's rows are written as pa_reshape_and_cache writes them
-  if (kv_dtype == PA_FP8_E4M3FN &&
+  if (quantised(kv_dtype) &&
       (!isfinite(k_scale) || !isfinite(v_scale) || k_scale == 0.0f || v_scale == 0.0f))
     return PA_ERR_BAD_SHAPE;
   return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, context_lens, num_seqs,
@@ -329,9 +334,9 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache
       num_blocks <= 0)
     return PA_ERR_BAD_SHAPE;
   if (!known_dtype(src_dtype) || !known_dtype(cache_dtype)) return PA_ERR_UNSUPPORTED;
-  if (src_dtype == PA_FP8_E4M3FN) return PA_ERR_UNSUPPORTED;
-  if (src_dtype != cache_dtype && cache_dtype != PA_FP8_E4M3FN) return PA_ERR_UNSUPPORTED;
-  if (cache_dtype == PA_FP8_E4M3FN && src_dtype != cache_dtype &&
+  if (quantised(src_dtype)) return PA_ERR_UNSUPPORTED;
+  if (src_dtype != cache_dtype && !quantised(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  if (quantised(cache_dtype) && src_dtype != cache_dtype &&
       (!isfinite(k_scale) || !isfinite(v_scale) || k_scale == 0.0f || v_scale == 0.0f))
     return PA_ERR_BAD_SHAPE;
   // rows are moved in 16-byte pieces of the source
@@ -418,7 +423,7 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int 
                                               int max_blocks_per_seq, int q_dtype) {
   if (num_seqs <= 0 || num_groups <= 0 || group_size <= 0 || num_q_heads <= 0 ||
       head_dim <= 0 || max_blocks_per_seq <= 0 || !known_dtype(q_dtype) ||
-      q_dtype == PA_FP8_E4M3FN)
+      quantised(q_dtype))
     return 0;
   return shared_prefix_layout(nullptr, num_seqs, num_groups, group_size, num_q_heads, head_dim,
                               max_blocks_per_seq, elem_bytes(q_dtype), pa::kMaxAutoSplits,

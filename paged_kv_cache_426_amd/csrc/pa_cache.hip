@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
     const int64_t slot = slot_mapping[t];
     if (slot < 0) return;
     uint8_t *dst = (is_v ? v_cache : k_cache) + (size_t)slot * row_elems * CB;
-    static_assert(CT == PA_FP8_E4M3FN, "only fp8 quantisation converts");
+    static_assert(CT == PA_FP8_E4M3FN || CT == PA_INT8, "only 8-bit caches convert");
+    auto enc = [](float v) { return CT == PA_INT8 ? f32_to_int8(v) : f32_to_e4m3fn(v); };
     const float scale = is_v ? v_scale : k_scale;
     for (int i = threadIdx.x; i < pieces; i += kCopyThreads) {
       const u32x4 w = reinterpret_cast<const u32x4 *>(src)[i];
@@ -75,10 +76,8 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
       for (int k = 0; k < VEC / 4; ++k) {
         // correctly rounded float32 division (the library is built with
         // -fhip-fp32-correctly-rounded-divide-sqrt and without fast-math)
-        packed[k] = f32_to_e4m3fn(x[4 * k] / scale) |
-                    (f32_to_e4m3fn(x[4 * k + 1] / scale) << 8) |
-                    (f32_to_e4m3fn(x[4 * k + 2] / scale) << 16) |
-                    (f32_to_e4m3fn(x[4 * k + 3] / scale) << 24);
+        packed[k] = enc(x[4 * k] / scale) | (enc(x[4 * k + 1] / scale) << 8) |
+                    (enc(x[4 * k + 2] / scale) << 16) | (enc(x[4 * k + 3] / scale) << 24);
       }
       if constexpr (VEC == 8) {
         reinterpret_cast<uint2 *>(dst)[i] = make_uint2(packed[0], packed[1]);
@@ -133,6 +132,9 @@ int launch_reshape_and_cache(const void *key, const void *value, void *k_cache, 
   PA_RC(PA_F32, PA_FP8_E4M3FN)
   PA_RC(PA_F16, PA_FP8_E4M3FN)
   PA_RC(PA_BF16, PA_FP8_E4M3FN)
+  PA_RC(PA_F32, PA_INT8)
+  PA_RC(PA_F16, PA_INT8)
+  PA_RC(PA_BF16, PA_INT8)
 #undef PA_RC
   return (int)e;
 }

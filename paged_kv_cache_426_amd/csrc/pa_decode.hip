@@ -151,6 +151,10 @@ KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, bool balan
   if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN)
     return large ? decode_kernels_bf16_fp8_large(d, gh, balanced, append)
                  : decode_kernels_bf16_fp8(d, gh, balanced, append);
+  if (q_dtype == PA_F16 && kv_dtype == PA_INT8 && !large)
+    return decode_kernels_f16_int8(d, gh, balanced, append);
+  if (q_dtype == PA_BF16 && kv_dtype == PA_INT8 && !large)
+    return decode_kernels_bf16_int8(d, gh, balanced, append);
   return {nullptr, 0};
 }
 
@@ -223,9 +227,10 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   const bool wide = p.mode == kSplitBalanced;
   p.direct = a.direct;
   p.group = a.num_q_heads / a.num_kv_heads;
-  const float ks = a.kv_dtype == PA_FP8_E4M3FN ? a.k_scale : 1.0f;
+  const bool q8 = a.kv_dtype == PA_FP8_E4M3FN || a.kv_dtype == PA_INT8;
+  const float ks = q8 ? a.k_scale : 1.0f;
   p.scale_log2 = a.scale * ks * kLog2e;
-  p.v_scale = a.kv_dtype == PA_FP8_E4M3FN ? a.v_scale : 1.0f;
+  p.v_scale = q8 ? a.v_scale : 1.0f;
   p.new_k = static_cast<const uint8_t *>(a.new_k);
   p.new_v = static_cast<const uint8_t *>(a.new_v);
   p.k_cache_w = const_cast<uint8_t *>(p.k_cache);

@@ -212,6 +212,11 @@ __device__ __forceinline__ void widen_v(const VPiece<KT> &pc, bool ok, float (&x
       x[2 * i] = f16_lo(w[i]);
       x[2 * i + 1] = f16_hi(w[i]);
     }
+  } else if constexpr (KT == PA_INT8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = (float)((int32_t)(w[i] << (24 - 8 * k)) >> 24);
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -235,6 +240,19 @@ __device__ __forceinline__ uint32_t fp8_pair_to_16(uint32_t w) {
   }
 }
 
+// int8 pair (bytes 0,1 or 2,3 of a word) widened exactly to the query's
+// 16-bit type: codes are integers of at most 8 significant bits.
+template <int QT, bool HI>
+__device__ __forceinline__ uint32_t int8_pair_to_16(uint32_t w) {
+  const float f0 = (float)((int32_t)(w << (HI ? 8 : 24)) >> 24);
+  const float f1 = (float)((int32_t)(w << (HI ? 0 : 16)) >> 24);
+  if constexpr (QT == PA_BF16) {
+    return (f2u(f0) >> 16) | (f2u(f1) & 0xffff0000u);
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1));
+  }
+}
+
 // B operand of MFMA step s from the lane's K loads of one block.
 template <int QT, int KT, int D>
 __device__ __forceinline__ typename QOpT<QT>::type k_operand(const u32x4 *k, int s) {
@@ -242,15 +260,22 @@ __device__ __forceinline__ typename QOpT<QT>::type k_operand(const u32x4 *k, int
     const u32x4 w = k[s / 4];
     const int t = s % 4;
     return u2f(t == 0 ? w.x : t == 1 ? w.y : t == 2 ? w.z : w.w);
-  } else if constexpr (KT == PA_FP8_E4M3FN) {
+  } else if constexpr (ElemBytes<KT>::value == 1) {
     const u32x4 w = k[s / 2];
     const uint32_t a = (s % 2) ? w.z : w.x;
     const uint32_t b = (s % 2) ? w.w : w.y;
     u32x4 r;
-    r.x = fp8_pair_to_16<QT, false>(a);
-    r.y = fp8_pair_to_16<QT, true>(a);
-    r.z = fp8_pair_to_16<QT, false>(b);
-    r.w = fp8_pair_to_16<QT, true>(b);
+    if constexpr (KT == PA_INT8) {
+      r.x = int8_pair_to_16<QT, false>(a);
+      r.y = int8_pair_to_16<QT, true>(a);
+      r.z = int8_pair_to_16<QT, false>(b);
+      r.w = int8_pair_to_16<QT, true>(b);
+    } else {
+      r.x = fp8_pair_to_16<QT, false>(a);
+      r.y = fp8_pair_to_16<QT, true>(a);
+      r.z = fp8_pair_to_16<QT, false>(b);
+      r.w = fp8_pair_to_16<QT, true>(b);
+    }
     return r;
   } else {
     return k[s];
@@ -336,10 +361,11 @@ struct AppendEnc {
   int blk, t, id;
 };
 
-// 8 source elements (16 bytes, 16-bit types) -> 8 fp8 e4m3fn bytes of
-// x / scale (round to nearest even, saturating), as the slot write does.
-template <int QT>
-__device__ __forceinline__ u32x2 fp8_of(const u32x4 &src, float scale) {
+// 8 source elements (16 bytes, 16-bit types) -> 8 cache bytes of x / scale
+// (fp8 e4m3fn or int8, round to nearest even, saturating), as the slot write
+// does.
+template <int QT, int KT>
+__device__ __forceinline__ u32x2 q8_of(const u32x4 &src, float scale) {
   const uint32_t w[4] = {src.x, src.y, src.z, src.w};
   float x[8];
 #pragma unroll
@@ -347,12 +373,12 @@ __device__ __forceinline__ u32x2 fp8_of(const u32x4 &src, float scale) {
     x[2 * i] = QT == PA_BF16 ? bf16_lo(w[i]) : f16_lo(w[i]);
     x[2 * i + 1] = QT == PA_BF16 ? bf16_hi(w[i]) : f16_hi(w[i]);
   }
+  auto enc = [](float v) { return KT == PA_INT8 ? f32_to_int8(v) : f32_to_e4m3fn(v); };
   uint32_t o[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    o[i] = f32_to_e4m3fn(x[4 * i] / scale) | (f32_to_e4m3fn(x[4 * i + 1] / scale) << 8) |
-           (f32_to_e4m3fn(x[4 * i + 2] / scale) << 16) |
-           (f32_to_e4m3fn(x[4 * i + 3] / scale) << 24);
+    o[i] = enc(x[4 * i] / scale) | (enc(x[4 * i + 1] / scale) << 8) |
+           (enc(x[4 * i + 2] / scale) << 16) | (enc(x[4 * i + 3] / scale) << 24);
   return u32x2{o[0], o[1]};
 }
 
@@ -367,8 +393,8 @@ __device__ __forceinline__ VPiece<KT> cache_vpiece(const u32x4 (&src)[N], float 
       pc.w[i] = (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
     }
   } else {
-    static_assert(KT == PA_FP8_E4M3FN && N == 1, "8 source elements of 16 bits");
-    const u32x2 o = fp8_of<QT>(src[0], scale);
+    static_assert(ElemBytes<KT>::value == 1 && N == 1, "8 source elements of 16 bits");
+    const u32x2 o = q8_of<QT, KT>(src[0], scale);
     pc.w[0] = o.x;
     pc.w[1] = o.y;
   }
@@ -382,7 +408,7 @@ __device__ __forceinline__ AppendEnc<QT, KT, D> encode_append(const AppendRow<QT
   if constexpr (QT == KT) {
     e.k = a.k;
   } else {
-    const u32x2 k8 = fp8_of<QT>(a.k, k_scale);
+    const u32x2 k8 = q8_of<QT, KT>(a.k, k_scale);
     e.k = u32x4{k8.x, k8.y, 0u, 0u};
   }
   e.v = cache_vpiece<QT, KT>(a.v, v_scale);
@@ -1103,5 +1129,7 @@ KernelRef decode_kernels_f16_f16_large(int d, int gh, bool balanced, bool append
 KernelRef decode_kernels_bf16_bf16_large(int d, int gh, bool balanced, bool append);
 KernelRef decode_kernels_f16_fp8_large(int d, int gh, bool balanced, bool append);
 KernelRef decode_kernels_bf16_fp8_large(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_f16_int8(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_bf16_int8(int d, int gh, bool balanced, bool append);
 
 }  // namespace pa

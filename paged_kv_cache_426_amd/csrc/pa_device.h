@@ -21,6 +21,7 @@ template <> struct ElemBytes<PA_F32> { static constexpr int value = 4; };
 template <> struct ElemBytes<PA_F16> { static constexpr int value = 2; };
 template <> struct ElemBytes<PA_BF16> { static constexpr int value = 2; };
 template <> struct ElemBytes<PA_FP8_E4M3FN> { static constexpr int value = 1; };
+template <> struct ElemBytes<PA_INT8> { static constexpr int value = 1; };
 
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -81,6 +82,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float f) {
   if (s > 25u) return sign;  // below 2^-11: rounds to zero
   const uint32_t q = (m + (1u << (s - 1u)) - 1u + ((m >> s) & 1u)) >> s;
   return sign | q;
+}
+
+// float32 -> symmetric int8 code (low byte of the result): round to
+// nearest, ties to even (v_rndne), saturating to [-127, 127]; NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_int8(float f) {
+  if (f != f) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(f), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xffu;
 }
 
 // ---------------------------------------------------------------------------

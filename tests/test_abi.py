@@ -82,6 +82,9 @@ def _decode(**kw):
     (dict(bs=256, NB=2 ** 28), 3),                 # 16-token sub-block ids exceed 32 bits
     (dict(qt=pa.PA_BF16, kt=pa.PA_F16), 3),        # mixed 16-bit types
     (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),  # fp8 cache needs a 16-bit query
+    (dict(qt=pa.PA_F32, kt=pa.PA_INT8), 3),        # int8 cache needs a 16-bit query
+    (dict(qt=pa.PA_BF16, kt=pa.PA_INT8, bs=32), 3),  # int8 decode: 16-token blocks only
+    (dict(qt=pa.PA_BF16, kt=pa.PA_INT8, vs=float("nan")), 2),
     (dict(qt=7), 3),
     (dict(P=24), 2),                               # not a multiple of block_size
     (dict(P=16), 1),                               # split without workspace
@@ -159,6 +162,10 @@ def test_reshape_and_copy_validation():
               pa.PA_FP8_E4M3FN, 1.0, 1.0, NULL) == 3
     assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, pa.PA_BF16, pa.PA_FP8_E4M3FN, 0.0,
               1.0, NULL) == 2                      # zero scale
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, pa.PA_BF16, pa.PA_INT8, 1.0,
+              float("inf"), NULL) == 2             # int8: finite scales
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, pa.PA_INT8, pa.PA_INT8, 1.0, 1.0,
+              NULL) == 3                           # int8 is a cache type only
     assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 3, 16, 4, pa.PA_F16, pa.PA_F16, 1.0, 1.0,
               NULL) == 3                           # row not a multiple of 16 bytes
     assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 64, 16, 4, pa.PA_F32, pa.PA_F32, 1.0, 1.0,

@@ -1,0 +1,143 @@
+"""int8 KV cache on the device against the oracle (the pages name INT8 KV
+storage beside FP8: "PagedAttention deep dive" section 4, "KV-Cache
+evolution" section 3C): the slot write's codes bit for bit (every rounding
+tie, saturation, NaN), block copies, decode over int8 caches for every split
+mode and query type, decode with append, and the long-context int8 batch."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_426_amd as pa
+import workloads as W
+from oracle.cache_ops import reshape_and_cache_bulk
+from _helpers import assert_close, device_inputs, device_step, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+EDGE_CTX = [1, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 255, 256, 257, 511, 512, 513, 1023, 1025]
+
+
+def _check(wl, P, what):
+    print(f"[int8] {what}", flush=True)
+    kc, vc, ref = oracle_step(wl)
+    d, out = device_step(wl, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy(d["k_cache"]), kc), f"{what}: k_cache after writes"
+    assert np.array_equal(W.to_numpy(d["v_cache"]), vc), f"{what}: v_cache after writes"
+    return assert_close(W.widen_to_f64(out), ref, wl.q_dtype, what)
+
+
+def test_int8_encoder_on_every_rounding_case():
+    """float32 source, scale 1: the stored code is the oracle's int8(x):
+    every half-integer tie in range and beyond, saturation, infinities, NaN."""
+    ties = np.arange(-140, 141, dtype=np.float32) + np.float32(0.5)
+    ints = np.arange(-140, 141, dtype=np.float32)
+    rng = np.random.default_rng(0)
+    x = np.concatenate([ties, ints, rng.uniform(-200, 200, 3000).astype(np.float32),
+                        np.array([np.inf, -np.inf, np.nan, -0.0, 1e-30, 126.49999],
+                                 dtype=np.float32)])
+    x = np.concatenate([x, np.zeros((-len(x)) % 64, np.float32)])
+    n = len(x) // 64
+    key = x.reshape(n, 1, 64)
+    nb = -(-n // 16)
+    dk = torch.zeros((nb, 16, 1, 64), dtype=torch.int8, device="cuda")
+    dv = torch.zeros_like(dk)
+    slots = W.to_device(np.arange(n, dtype=np.int64))
+    pa.reshape_and_cache(W.to_device(key), W.to_device(key), dk, dv, slots, 1.0, 1.0)
+    got = W.to_numpy(dk).reshape(-1)[: len(x)]
+    expect = oracle.int8_encode(x)
+    bad = np.nonzero(got != expect)[0]
+    assert len(bad) == 0, f"{len(bad)} mismatches, e.g. x={x[bad[:5]]} got {got[bad[:5]]}"
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16", "f32"])
+def test_slot_write_int8_quantise(src):
+    rng = np.random.default_rng(12)
+    hkv, d, bs, nb, n = 8, 128, 16, 9, 60
+    kc = rng.integers(-128, 128, (nb, bs, hkv, d)).astype(np.int8)
+    vc = rng.integers(-128, 128, (nb, bs, hkv, d)).astype(np.int8)
+    key = W.configs.normal(rng, (n, hkv, d), src)
+    val = W.configs.normal(rng, (n, hkv, d), src)
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    slots[0] = -1
+    ks, vs = 0.0123, 0.0071                       # some values saturate at 127
+    ek, ev = kc.copy(), vc.copy()
+    reshape_and_cache_bulk(key, val, ek, ev, slots, ks, vs)
+    dk, dv = W.to_device(kc), W.to_device(vc)
+    pa.reshape_and_cache(W.to_device(key), W.to_device(val), dk, dv, W.to_device(slots), ks, vs)
+    assert np.array_equal(W.to_numpy(dk), ek)
+    assert np.array_equal(W.to_numpy(dv), ev)
+
+
+def test_copy_blocks_int8():
+    rng = np.random.default_rng(3)
+    kc = rng.integers(-128, 128, (20, 16, 8, 128)).astype(np.int8)
+    vc = rng.integers(-128, 128, (20, 16, 8, 128)).astype(np.int8)
+    pairs = np.array([[3, 7], [3, 11], [0, 19]], dtype=np.int64)
+    ek, ev = kc.copy(), vc.copy()
+    oracle.copy_blocks(ek, ev, pairs)
+    dk, dv = W.to_device(kc), W.to_device(vc)
+    pa.copy_blocks(dk, dv, W.to_device(pairs))
+    assert np.array_equal(W.to_numpy(dk), ek) and np.array_equal(W.to_numpy(dv), ev)
+
+
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("P", [0, 16, 256, -1, -5])
+def test_int8_edge_lengths(q_dtype, d, P):
+    wl = W.custom(EDGE_CTX, 8, 2, d, q_dtype=q_dtype, kv_dtype="int8", seed=d + abs(P))
+    _check(wl, P, f"{q_dtype}/int8 d={d} P={P}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (12, 4), (16, 1), (32, 8), (32, 1)])
+@pytest.mark.parametrize("P", [0, 64, -1, -3])
+def test_int8_gqa_groups(Hq, Hkv, P):
+    wl = W.custom([5, 100, 700], Hq, Hkv, 128, q_dtype="bf16", kv_dtype="int8", seed=Hq * Hkv)
+    _check(wl, P, f"int8 Hq={Hq} Hkv={Hkv} P={P}")
+
+
+@pytest.mark.parametrize("P", [0, -1, 32])
+def test_int8_decode_append_equals_write_then_decode(P):
+    wl = W.custom(EDGE_CTX, 32, 8, 128, q_dtype="bf16", kv_dtype="int8", seed=41)
+    d = device_inputs(wl)
+    pa.reshape_and_cache(d["hist_key"], d["hist_value"], d["k_cache"], d["v_cache"],
+                         d["hist_slots"], wl.k_scale, wl.v_scale)
+    kw = dict(scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale, partition_size=P)
+    k1, v1 = d["k_cache"].clone(), d["v_cache"].clone()
+    pa.reshape_and_cache(d["new_key"], d["new_value"], k1, v1, d["new_slots"], wl.k_scale,
+                         wl.v_scale)
+    sep = pa.decode(d["q"], k1, v1, d["block_tables"], d["context_lens"], **kw)
+    k2, v2 = d["k_cache"].clone(), d["v_cache"].clone()
+    fused = pa.decode_append(d["q"], d["new_key"], d["new_value"], k2, v2, d["block_tables"],
+                             d["context_lens"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert torch.equal(sep, fused)
+
+
+def test_int8_large_blocks_are_refused():
+    wl = W.custom([40], 8, 2, 128, q_dtype="bf16", kv_dtype="int8", bs=32, seed=1)
+    d = device_inputs(wl)
+    with pytest.raises(pa.PaError):
+        pa.decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                  k_scale=wl.k_scale, v_scale=wl.v_scale)
+
+
+def test_long_ctx_int8_b8():
+    """The long-context batch with an int8 cache, at the benchmark's launch
+    configuration (512-token partitions) and the balanced split, on the
+    shortest and the longest sequence."""
+    wl = W.build("long_ctx_int8_b8")
+    seqs = [int(np.argmin(wl.context_lens)), int(np.argmax(wl.context_lens))]
+    kc, vc, ref = oracle_step(wl, seqs=seqs)
+    for P in (wl.partition_size, -1):
+        print(f"[int8] long_ctx_int8_b8 P={P}", flush=True)
+        d, out = device_step(wl, P)
+        torch.cuda.synchronize()
+        blocks = np.unique(np.concatenate([
+            wl.block_tables[b, : -(-int(wl.context_lens[b]) // wl.block_size)] for b in seqs]))
+        assert np.array_equal(W.to_numpy(d["k_cache"])[blocks], kc[blocks])
+        assert np.array_equal(W.to_numpy(d["v_cache"])[blocks], vc[blocks])
+        assert_close(W.widen_to_f64(out), ref, wl.q_dtype, f"long_ctx_int8_b8 P={P}")

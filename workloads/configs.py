@@ -28,8 +28,11 @@ import numpy as np
 
 from .blockpool import BlockPool
 
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3fn": np.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3fn": np.uint8,
+           "int8": np.int8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1, "int8": 1}
+# 8-bit cache types: filled through the slot write with scale amax|x| / CODE_MAX
+CODE_MAX = {"fp8_e4m3fn": 448.0, "int8": 127.0}
 
 
 def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -305,7 +308,8 @@ def shared_prefix_cow_b64(seed: int = 4, partition_size: int = -1, groups: int =
 
 
 def long_ctx_fp8_b8(seed: int = 5, partition_size: int = 512, batch: int = 8,
-                    ctx_lo: int = 16384, ctx_hi: int = 32768) -> Workload:
+                    ctx_lo: int = 16384, ctx_hi: int = 32768,
+                    kv_dtype: str = "fp8_e4m3fn") -> Workload:
     """Long contexts with an fp8 cache: batch 8, context lengths uniform on
     [16384, 32768], 32 query / 8 KV heads, head_dim 128, bf16 queries, K/V
     stored as OCP E4M3FN with one float32 scale per tensor, block_size 16,
@@ -315,6 +319,8 @@ def long_ctx_fp8_b8(seed: int = 5, partition_size: int = 512, batch: int = 8,
     written through the slot write, which quantises it; the pool starts as
     zeros. Each scale is amax|x| / 448 over that tensor's bf16 values
     (448 being the largest E4M3FN magnitude), rounded to float32.
+    With kv_dtype "int8" the cache holds symmetric int8 codes instead, with
+    scale amax|x| / 127 (the same workload otherwise).
     """
     rng = np.random.default_rng(seed)
     Hq, Hkv, d, bs = 32, 8, 128, 16
@@ -334,12 +340,13 @@ def long_ctx_fp8_b8(seed: int = 5, partition_size: int = 512, batch: int = 8,
 
     def amax_scale(*parts):
         m = max(float(np.abs(_bf16_as_f32(p)).max()) for p in parts)
-        return float(np.float32(np.float32(m) / np.float32(448.0)))
+        return float(np.float32(np.float32(m) / np.float32(CODE_MAX[kv_dtype])))
 
-    zeros = np.zeros((needed, bs, Hkv, d), dtype=np.uint8)
+    zeros = np.zeros((needed, bs, Hkv, d), dtype=STORAGE[kv_dtype])
     return Workload(
-        name="long_ctx_fp8_b8", num_seqs=batch, num_q_heads=Hq, num_kv_heads=Hkv,
-        head_dim=d, block_size=bs, num_blocks=needed, q_dtype="bf16", kv_dtype="fp8_e4m3fn",
+        name="long_ctx_fp8_b8" if kv_dtype == "fp8_e4m3fn" else f"long_ctx_{kv_dtype}_b8",
+        num_seqs=batch, num_q_heads=Hq, num_kv_heads=Hkv,
+        head_dim=d, block_size=bs, num_blocks=needed, q_dtype="bf16", kv_dtype=kv_dtype,
         q=q, k_cache=zeros, v_cache=zeros.copy(),
         block_tables=_tables(seqs, 32768 // bs), context_lens=ctx,
         scale=float(np.float32(1.0 / math.sqrt(d))),
@@ -361,6 +368,7 @@ BUILDERS = {
     "mha_b32_ctx4096": mha_b32_ctx4096,
     "shared_prefix_cow_b64": shared_prefix_cow_b64,
     "long_ctx_fp8_b8": long_ctx_fp8_b8,
+    "long_ctx_int8_b8": lambda **kw: long_ctx_fp8_b8(**{"kv_dtype": "int8", **kw}),
 }
 
 
@@ -395,10 +403,10 @@ def custom(ctx_lens, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16", bs=16, seed=0,
         slots.append(slot)
     B = len(ctx_lens)
     mbs = mbs or max(1, max(-(-int(n) // bs) for n in ctx_lens))
-    store_kv = kv_dtype if kv_dtype != "fp8_e4m3fn" else None
+    store_kv = kv_dtype if kv_dtype not in CODE_MAX else None
     if store_kv is None:
-        k_cache = np.zeros((nb, bs, Hkv, d), np.uint8)
-        v_cache = np.zeros((nb, bs, Hkv, d), np.uint8)
+        k_cache = np.zeros((nb, bs, Hkv, d), STORAGE[kv_dtype])
+        v_cache = np.zeros((nb, bs, Hkv, d), STORAGE[kv_dtype])
         hist_slots = np.concatenate([
             _slots_of_positions(s.block_table, np.arange(int(n) - 1), bs)
             for s, n in zip(seqs, ctx_lens) if n > 1] or [np.zeros(0, np.int64)])
@@ -428,10 +436,11 @@ def custom(ctx_lens, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16", bs=16, seed=0,
                    for a in (hist_key, new_key)]
         parts_v = [_bf16_as_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
                    for a in (hist_value, new_value)]
+        cmax = np.float32(CODE_MAX[kv_dtype])
         wl.k_scale = float(np.float32(np.float32(max(np.abs(p).max() for p in parts_k if p.size))
-                                      / np.float32(448.0)))
+                                      / cmax))
         wl.v_scale = float(np.float32(np.float32(max(np.abs(p).max() for p in parts_v if p.size))
-                                      / np.float32(448.0)))
+                                      / cmax))
     return wl
 
 
