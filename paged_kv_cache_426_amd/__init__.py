@@ -16,7 +16,11 @@ from typing import Optional, Tuple
 
 import torch
 
+from . import checks
+from .checks import ContractError, set_debug_checks
+
 __all__ = [
+    "ContractError", "set_debug_checks",
     "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN", "PA_INT8",
     "PaError", "lib", "library_path", "dtype_code",
     "decode", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
@@ -181,6 +185,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Paged-attention decode (C: pa_decode). Returns out [B, Hq, d] in q's type."""
     dev = _dev(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -220,10 +226,14 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     dev = _dev(q, k_cache, v_cache, block_tables, context_lens, group_members, prefix_lens, out,
                workspace)
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
     if group_members.dim() != 2 or prefix_lens.shape != (group_members.shape[0],):
         raise PaError("group_members must be [G, M] and prefix_lens [G]")
     _i32(group_members, "group_members")
     _i32(prefix_lens, "prefix_lens")
+    if checks.debug_checks_enabled():
+        checks.check_shared_prefix(block_tables, context_lens, group_members, prefix_lens, bs)
     G, M = group_members.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -254,6 +264,8 @@ def decode_append(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     position, then out = decode over the caches. Returns out [B, Hq, d]."""
     dev = _dev(q, key, value, k_cache, v_cache, block_tables, context_lens, out, workspace)
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
     if key.shape != (B, Hkv, d) or value.shape != key.shape or key.dtype != q.dtype or \
             value.dtype != q.dtype:
         raise PaError("key and value must be [B, Hkv, d] in q's type")
@@ -287,6 +299,8 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, partition_s
     tmp_out [Hq, S + B, d], max_logits and exp_sums [Hq, S + B]."""
     dev = _dev(q, k_cache, v_cache, block_tables, context_lens, tmp_out, max_logits, exp_sums)
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     lead = (B, Hq) if partition_size > 0 else (Hq,)
@@ -347,6 +361,8 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
         raise PaError("expected key/value [N, Hkv, d], caches [num_blocks, bs, Hkv, d], slots [N]")
     N, Hkv, d = key.shape
     NB, bs = k_cache.shape[:2]
+    if checks.debug_checks_enabled():
+        checks.check_slot_mapping(slot_mapping, NB, bs)
     _check(lib().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(slot_mapping), N, Hkv, d, bs, NB, dtype_code(key),
                                       dtype_code(k_cache), float(k_scale), float(v_scale),
@@ -361,6 +377,8 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
             v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise PaError("expected caches [num_blocks, bs, Hkv, d] and block_mapping [P, 2]")
     NB, bs, Hkv, d = k_cache.shape
+    if checks.debug_checks_enabled():
+        checks.check_block_mapping(block_mapping, NB)
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
                                 block_mapping.shape[0], Hkv, d, bs, NB, dtype_code(k_cache),
                                 _stream(dev)))

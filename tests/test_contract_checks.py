@@ -1,0 +1,124 @@
+"""The host-side checker of device-data preconditions (block ids, context
+lengths, slots, copy pairs, prefix groups): accepts the workloads as built,
+rejects each kind of breach, and runs before binding calls when debug
+checks are on. CPU only: the checks read host copies of the index tensors."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_426_amd as pa
+import workloads as W
+from paged_kv_cache_426_amd import checks
+from paged_kv_cache_426_amd.checks import ContractError
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_gqa2", "shared_prefix_cow_b64"])
+def test_workloads_pass(name):
+    wl = W.build(name)
+    checks.check_decode(wl.block_tables, wl.context_lens, wl.num_blocks, wl.block_size)
+    checks.check_slot_mapping(wl.new_slots, wl.num_blocks, wl.block_size)
+    checks.check_block_mapping(wl.cow_pairs, wl.num_blocks)
+    if wl.prefix_members is not None:
+        checks.check_shared_prefix(wl.block_tables, wl.context_lens, wl.prefix_members,
+                                   wl.prefix_lens, wl.block_size)
+
+
+def test_decode_breaches():
+    bt = np.array([[3, 1, 7], [2, 9, 0]], dtype=np.int32)
+    cl = np.array([40, 20], dtype=np.int32)
+    checks.check_decode(bt, cl, 10, 16)                       # entries past ceil(n/16) unread
+    with pytest.raises(ContractError, match="outside"):
+        checks.check_decode(bt, cl, 9, 16)                    # block 9 in a pool of 9
+    with pytest.raises(ContractError, match="context_lens"):
+        checks.check_decode(bt, np.array([49, 20], np.int32), 10, 16)   # 3 x 16 = 48 tokens
+    with pytest.raises(ContractError, match="context_lens"):
+        checks.check_decode(bt, np.array([-1, 20], np.int32), 10, 16)
+    bt2 = bt.copy()
+    bt2[1, 1] = -4
+    with pytest.raises(ContractError, match=r"block_tables\[1\]\[1\]"):
+        checks.check_decode(bt2, cl, 10, 16)
+
+
+def test_slot_and_copy_breaches():
+    checks.check_slot_mapping(np.array([5, -1, 17, -1]), 2, 16)
+    with pytest.raises(ContractError, match="twice"):
+        checks.check_slot_mapping(np.array([5, 5]), 2, 16)
+    with pytest.raises(ContractError, match="beyond"):
+        checks.check_slot_mapping(np.array([32]), 2, 16)
+    checks.check_block_mapping(np.array([[1, 4], [1, 5]]), 6)  # one source, two copies
+    with pytest.raises(ContractError, match="destination of two"):
+        checks.check_block_mapping(np.array([[1, 4], [2, 4]]), 6)
+    with pytest.raises(ContractError, match="source and a destination"):
+        checks.check_block_mapping(np.array([[1, 4], [4, 5]]), 6)
+    with pytest.raises(ContractError, match="outside"):
+        checks.check_block_mapping(np.array([[1, 6]]), 6)
+
+
+def test_shared_prefix_breaches():
+    bt = np.array([[5, 6, 7, 0], [5, 6, 8, 0], [5, 9, 3, 0]], dtype=np.int32)
+    cl = np.array([40, 40, 33], dtype=np.int32)
+    gm = np.array([[0, 1], [2, -1]], dtype=np.int32)
+    checks.check_shared_prefix(bt, cl, gm, np.array([32, 16], np.int32), 16)
+    with pytest.raises(ContractError, match="different blocks"):
+        checks.check_shared_prefix(bt, cl, np.array([[0, 2]], np.int32), np.array([32], np.int32), 16)
+    with pytest.raises(ContractError, match="more than one slot"):
+        checks.check_shared_prefix(bt, cl, np.array([[0, 1], [1, -1]], np.int32),
+                                   np.array([16, 16], np.int32), 16)
+    with pytest.raises(ContractError, match="fewer"):
+        checks.check_shared_prefix(bt, np.array([40, 20, 33], np.int32), gm,
+                                   np.array([32, 16], np.int32), 16)
+    with pytest.raises(ContractError, match="outside"):
+        checks.check_shared_prefix(bt, cl, np.array([[0, 3]], np.int32), np.array([16], np.int32), 16)
+
+
+def test_binding_runs_the_checks_when_enabled(monkeypatch):
+    """With debug checks on, a binding call with a breach raises before the
+    library is reached (CPU tensors would be refused later anyway)."""
+    wl = W.build("tiny_fp32_gqa2")
+    q = torch.from_numpy(wl.q)
+    kc = torch.from_numpy(wl.k_cache)
+    bt = torch.from_numpy(wl.block_tables.copy())
+    bt[0, 0] = wl.num_blocks                        # out of the pool
+    cl = torch.from_numpy(wl.context_lens)
+    monkeypatch.setattr(pa, "_dev", lambda *a: torch.device("cpu"))
+    pa.set_debug_checks(True)
+    try:
+        with pytest.raises(ContractError):
+            pa.decode(q, kc, kc, bt, cl)
+        with pytest.raises(ContractError):
+            pa.copy_blocks(kc, kc, torch.tensor([[1, 2], [3, 2]], dtype=torch.int64))
+        with pytest.raises(ContractError):
+            pa.reshape_and_cache(q[:, :2], q[:, :2], kc, kc, torch.tensor([1, 1]))
+    finally:
+        pa.set_debug_checks(False)
+    assert not checks.debug_checks_enabled()
+
+
+@pytest.mark.gpu
+def test_checks_on_device_tensors_change_nothing():
+    """With debug checks on, a full step through the binding on device
+    tensors (the checks copy the index tensors to the host) gives bitwise
+    the output and caches of the same step with the checks off."""
+    from _helpers import device_step
+
+    wl = W.build("shared_prefix_cow_b64", groups=2, samples=3, prompt=40, parent_decoded=5,
+                 private=20, Hq=8, Hkv=2, d=128)
+    d0, out0 = device_step(wl, -1)
+    pa.set_debug_checks(True)
+    try:
+        d1, out1 = device_step(wl, -1)
+        gm = torch.as_tensor(wl.prefix_members, dtype=torch.int32, device="cuda")
+        pl = torch.as_tensor(wl.prefix_lens, dtype=torch.int32, device="cuda")
+        sp = pa.decode_shared_prefix(d1["q"], d1["k_cache"], d1["v_cache"], d1["block_tables"],
+                                     d1["context_lens"], gm, pl, scale=wl.scale)
+        bad = d1["block_tables"].clone()
+        bad[0, 0] = wl.num_blocks
+        with pytest.raises(ContractError):
+            pa.decode(d1["q"], d1["k_cache"], d1["v_cache"], bad, d1["context_lens"])
+    finally:
+        pa.set_debug_checks(False)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    assert torch.equal(d0["k_cache"], d1["k_cache"]) and torch.equal(d0["v_cache"], d1["v_cache"])
+    assert torch.isfinite(sp.float()).all()
