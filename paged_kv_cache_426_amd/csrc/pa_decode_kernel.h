@@ -296,6 +296,29 @@ __device__ __forceinline__ f32x4 mfma(typename QOpT<QT>::type a, typename QOpT<Q
   }
 }
 
+// 16x16x16 MFMA on 16-bit operands (four per lane, as two packed words):
+// lane l holds A[l % 16][4 (l / 16) + 0..3] and B[4 (l / 16) + 0..3][l % 16],
+// and gets D[4 (l / 16) + 0..3][l % 16].
+template <int QT>
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  if constexpr (QT == PA_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+}
+
+// two fp32 values -> the query's 16-bit type (round to nearest even), packed
+template <int QT>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (QT == PA_BF16) return f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  else return f32_to_f16_rne(lo) | ((uint32_t)f32_to_f16_rne(hi) << 16);
+}
+
 template <int QT>
 __device__ __forceinline__ void store_elem(void *out, size_t idx, float v) {
   if constexpr (QT == PA_F32) {
@@ -616,17 +639,33 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 
   // ---- per-wave softmax state ----------------------------------------------
   float m[4], l[4];
-  float acc[GH][8];
+  // P.V on MFMA for 16 query heads of a 128-wide head (16-bit queries, one
+  // block per unit): a 16x16x16 product per 16 output columns replaces the
+  // 16 x 8 fp32 FMAs per V element, which bind the vector ALU at 16 rows.
+  // Lane (r, c) of the V layout holds tokens 4i + r (i = 0..3), elements
+  // [8c, 8c + 8): MFMA t takes those four tokens as its k = 4r .. 4r + 3 and
+  // element 8c + t as column c, so its output column c is element 8c + t of
+  // the rows' P.V; the probabilities go through LDS in the same token order.
+  // Output rows are heads 4 (l / 16) + j, the rows this lane's softmax state
+  // already holds, so the rescale needs no exchange.
+  constexpr bool PVM = GH == 16 && D == 128 && QT != PA_F32 && NBI == 1;
+  float acc[PVM ? 1 : GH][8];
+  f32x4 acc2[PVM ? 8 : 1];
   auto reset = [&]() {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       m[v] = -INFINITY;
       l[v] = 0.0f;
     }
+    if constexpr (PVM) {
 #pragma unroll
-    for (int h = 0; h < GH; ++h)
+      for (int t = 0; t < 8; ++t) acc2[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+      for (int h = 0; h < GH; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    }
   };
 
   const uint32_t rowstride = (uint32_t)p.num_kv_heads * G::row;
@@ -747,6 +786,58 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       }
     }
     wave_lds_fence();
+    if constexpr (PVM) {
+      // rows 4 jq + j of acc2 are this lane's softmax rows: alpha in hand
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        acc2[t].x *= al[0];
+        acc2[t].y *= al[1];
+        acc2[t].z *= al[2];
+        acc2[t].w *= al[3];
+      }
+      // A: P[head tl][tokens 4i + jq], i = 0..3
+      float pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = sh.p[wave][4 * i + jq][tl];
+      const u32x2 aop = {pack16<QT>(pk[0], pk[1]), pack16<QT>(pk[2], pk[3])};
+      // B: the lane's V pieces (tokens 4i + r), the appended row in place of
+      // the cache's, masked tokens zero
+      const bool newblk = APP && app.blk == jb;
+      const VPiece<KT> &vp = app.v;
+      VPiece<KT> pcs[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = 4 * i + r;
+        const uint32_t keep = jb * kBs + tk < tok_lim ? ~0u : 0u;
+        const uint32_t mk = (newblk && tk == app.t) ? ~0u : 0u;
+#pragma unroll
+        for (int w = 0; w < 2 * ElemBytes<KT>::value; ++w)
+          pcs[i].w[w] = ((vp.w[w] & mk) | (st.v[0][i].w[w] & ~mk)) & keep;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        u32x2 bop;
+        if constexpr (ElemBytes<KT>::value == 2) {
+          // element t of tokens (i0, i1): its 16-bit halves side by side
+          const uint32_t sel = (t % 2) ? 0x07060302u : 0x05040100u;
+          bop.x = __builtin_amdgcn_perm(pcs[1].w[t / 2], pcs[0].w[t / 2], sel);
+          bop.y = __builtin_amdgcn_perm(pcs[3].w[t / 2], pcs[2].w[t / 2], sel);
+        } else {
+          // byte t of tokens (i0, i1) into bytes 0, 1, widened exactly
+          const uint32_t sel = 0x0c0c0000u | ((4u + t % 4) << 8) | (uint32_t)(t % 4);
+          const uint32_t w01 = __builtin_amdgcn_perm(pcs[1].w[t / 4], pcs[0].w[t / 4], sel);
+          const uint32_t w23 = __builtin_amdgcn_perm(pcs[3].w[t / 4], pcs[2].w[t / 4], sel);
+          if constexpr (KT == PA_INT8) {
+            bop.x = int8_pair_to_16<QT, false>(w01);
+            bop.y = int8_pair_to_16<QT, false>(w23);
+          } else {
+            bop.x = fp8_pair_to_16<QT, false>(w01);
+            bop.y = fp8_pair_to_16<QT, false>(w23);
+          }
+        }
+        acc2[t] = mfma16<QT>(aop, bop, acc2[t]);
+      }
+    } else {
     {
       float a[GH];
 #pragma unroll
@@ -786,6 +877,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
           for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], x[e], acc[h][e]);
       }
     }
+    }
     wave_lds_fence();
   };
 
@@ -803,17 +895,28 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
           sh.l[wave][4 * jq + v] = l[v];
         }
     }
+    if constexpr (PVM) {
+      // acc2[t] holds heads 4 jq + j, element 8 tl + t: whole sums
   #pragma unroll
-    for (int h = 0; h < GH; ++h)
-  #pragma unroll
-      for (int e = 0; e < 8; ++e)
-  #pragma unroll
-        for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
-    if (r == 0) {
+      for (int t = 0; t < 8; ++t) {
+        sh.acc[wave][4 * jq + 0][8 * tl + t] = acc2[t].x;
+        sh.acc[wave][4 * jq + 1][8 * tl + t] = acc2[t].y;
+        sh.acc[wave][4 * jq + 2][8 * tl + t] = acc2[t].z;
+        sh.acc[wave][4 * jq + 3][8 * tl + t] = acc2[t].w;
+      }
+    } else {
   #pragma unroll
       for (int h = 0; h < GH; ++h)
   #pragma unroll
-        for (int e = 0; e < 8; ++e) sh.acc[wave][h][c * 8 + e] = acc[h][e];
+        for (int e = 0; e < 8; ++e)
+  #pragma unroll
+          for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
+      if (r == 0) {
+  #pragma unroll
+        for (int h = 0; h < GH; ++h)
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) sh.acc[wave][h][c * 8 + e] = acc[h][e];
+      }
     }
     __syncthreads();
 
