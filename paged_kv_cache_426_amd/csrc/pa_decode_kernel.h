@@ -312,11 +312,21 @@ __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
   }
 }
 
-// two fp32 values -> the query's 16-bit type (round to nearest even), packed
+// Two fp32 values as a sum of two values of the query's 16-bit type each,
+// packed in pairs: hi = round(x) (nearest even), lo = round(x - hi), where
+// x - hi is exact in fp32. hi + lo carries about 16 significant bits, so a
+// product over such pairs is as accurate as fp32 accumulation needs.
 template <int QT>
-__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
-  if constexpr (QT == PA_BF16) return f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-  else return f32_to_f16_rne(lo) | ((uint32_t)f32_to_f16_rne(hi) << 16);
+__device__ __forceinline__ void split16(float a, float b, uint32_t &hi, uint32_t &lo) {
+  if constexpr (QT == PA_BF16) {
+    const uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b);
+    hi = ha | (hb << 16);
+    lo = f32_to_bf16_rne(a - u2f(ha << 16)) | ((uint32_t)f32_to_bf16_rne(b - u2f(hb << 16)) << 16);
+  } else {
+    const uint32_t ha = f32_to_f16_rne(a), hb = f32_to_f16_rne(b);
+    hi = ha | (hb << 16);
+    lo = f32_to_f16_rne(a - f16_lo(ha)) | ((uint32_t)f32_to_f16_rne(b - f16_lo(hb)) << 16);
+  }
 }
 
 template <int QT>
@@ -639,16 +649,18 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 
   // ---- per-wave softmax state ----------------------------------------------
   float m[4], l[4];
-  // P.V on MFMA for 16 query heads of a 128-wide head (16-bit queries, one
-  // block per unit): a 16x16x16 product per 16 output columns replaces the
-  // 16 x 8 fp32 FMAs per V element, which bind the vector ALU at 16 rows.
+  // P.V on MFMA for 4 to 16 query heads of a 128-wide head (16-bit queries,
+  // one block per unit): 16x16x16 products per 16 output columns replace the
+  // GH x 8 fp32 FMAs per V element on the vector ALU (rows past GH repeat
+  // the first GH, as in the logits tile).
   // Lane (r, c) of the V layout holds tokens 4i + r (i = 0..3), elements
   // [8c, 8c + 8): MFMA t takes those four tokens as its k = 4r .. 4r + 3 and
   // element 8c + t as column c, so its output column c is element 8c + t of
-  // the rows' P.V; the probabilities go through LDS in the same token order.
+  // the rows' P.V; the probabilities go through LDS in the same token order
+  // and enter as two 16-bit parts (split16), V exactly.
   // Output rows are heads 4 (l / 16) + j, the rows this lane's softmax state
   // already holds, so the rescale needs no exchange.
-  constexpr bool PVM = GH == 16 && D == 128 && QT != PA_F32 && NBI == 1;
+  constexpr bool PVM = GH >= 4 && D == 128 && QT != PA_F32 && NBI == 1;
   float acc[PVM ? 1 : GH][8];
   f32x4 acc2[PVM ? 8 : 1];
   auto reset = [&]() {
@@ -798,8 +810,11 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       // A: P[head tl][tokens 4i + jq], i = 0..3
       float pk[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = sh.p[wave][4 * i + jq][tl];
-      const u32x2 aop = {pack16<QT>(pk[0], pk[1]), pack16<QT>(pk[2], pk[3])};
+      for (int i = 0; i < 4; ++i) pk[i] = sh.p[wave][4 * i + jq][tl % GH];
+      uint32_t h0, l0, h1, l1;  // probabilities, high and low parts
+      split16<QT>(pk[0], pk[1], h0, l0);
+      split16<QT>(pk[2], pk[3], h1, l1);
+      const u32x2 aop = {h0, h1}, aol = {l0, l1};
       // B: the lane's V pieces (tokens 4i + r), the appended row in place of
       // the cache's, masked tokens zero
       const bool newblk = APP && app.blk == jb;
@@ -836,6 +851,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
           }
         }
         acc2[t] = mfma16<QT>(aop, bop, acc2[t]);
+        acc2[t] = mfma16<QT>(aol, bop, acc2[t]);
       }
     } else {
     {
@@ -896,13 +912,16 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         }
     }
     if constexpr (PVM) {
-      // acc2[t] holds heads 4 jq + j, element 8 tl + t: whole sums
+      // acc2[t] holds heads (4 jq + j) % GH, element 8 tl + t: whole sums
+      // (rows past GH repeat the first GH)
+      if (4 * jq < GH) {
   #pragma unroll
       for (int t = 0; t < 8; ++t) {
         sh.acc[wave][4 * jq + 0][8 * tl + t] = acc2[t].x;
         sh.acc[wave][4 * jq + 1][8 * tl + t] = acc2[t].y;
         sh.acc[wave][4 * jq + 2][8 * tl + t] = acc2[t].z;
         sh.acc[wave][4 * jq + 3][8 * tl + t] = acc2[t].w;
+      }
       }
     } else {
   #pragma unroll
