@@ -854,45 +854,45 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         acc2[t] = mfma16<QT>(aol, bop, acc2[t]);
       }
     } else {
-    {
-      float a[GH];
+      {
+        float a[GH];
 #pragma unroll
-      for (int h = 0; h < GH; ++h) a[h] = sh.alpha[wave][h];
-#pragma unroll
-      for (int h = 0; h < GH; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= a[h];
-    }
-#pragma unroll
-    for (int bi = 0; bi < NBI; ++bi) {
-      // the appended token's V piece, for the lanes holding its row
-      const bool newblk = APP && app.blk == jb + bi;
-      const VPiece<KT> &vp = app.v;
-#pragma unroll
-      for (int i = 0; i < G::nvl; ++i) {
-        const int t = i * G::rv + r;
-        const bool ok = (jb + bi) * kBs + t < tok_lim;
-        float x[8];
-        if (newblk) {
-          // (a mask, not a select of references: both pieces stay in registers)
-          const uint32_t mk = t == app.t ? ~0u : 0u;
-          VPiece<KT> pc;
-#pragma unroll
-          for (int w = 0; w < 2 * ElemBytes<KT>::value; ++w)
-            pc.w[w] = (vp.w[w] & mk) | (st.v[bi][i].w[w] & ~mk);
-          widen_v<KT>(pc, ok, x);
-        } else {
-          widen_v<KT>(st.v[bi][i], ok, x);
-        }
-        float pw[GH];
-#pragma unroll
-        for (int h = 0; h < GH; ++h) pw[h] = sh.p[wave][bi * kBs + t][h];
+        for (int h = 0; h < GH; ++h) a[h] = sh.alpha[wave][h];
 #pragma unroll
         for (int h = 0; h < GH; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], x[e], acc[h][e]);
+          for (int e = 0; e < 8; ++e) acc[h][e] *= a[h];
       }
-    }
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi) {
+        // the appended token's V piece, for the lanes holding its row
+        const bool newblk = APP && app.blk == jb + bi;
+        const VPiece<KT> &vp = app.v;
+#pragma unroll
+        for (int i = 0; i < G::nvl; ++i) {
+          const int t = i * G::rv + r;
+          const bool ok = (jb + bi) * kBs + t < tok_lim;
+          float x[8];
+          if (newblk) {
+            // (a mask, not a select of references: both pieces stay in registers)
+            const uint32_t mk = t == app.t ? ~0u : 0u;
+            VPiece<KT> pc;
+#pragma unroll
+            for (int w = 0; w < 2 * ElemBytes<KT>::value; ++w)
+              pc.w[w] = (vp.w[w] & mk) | (st.v[bi][i].w[w] & ~mk);
+            widen_v<KT>(pc, ok, x);
+          } else {
+            widen_v<KT>(st.v[bi][i], ok, x);
+          }
+          float pw[GH];
+#pragma unroll
+          for (int h = 0; h < GH; ++h) pw[h] = sh.p[wave][bi * kBs + t][h];
+#pragma unroll
+          for (int h = 0; h < GH; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], x[e], acc[h][e]);
+        }
+      }
     }
     wave_lds_fence();
   };
