@@ -316,16 +316,22 @@ __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
 // packed in pairs: hi = round(x) (nearest even), lo = round(x - hi), where
 // x - hi is exact in fp32. hi + lo carries about 16 significant bits, so a
 // product over such pairs is as accurate as fp32 accumulation needs.
+// (The casts compile to the hardware's packed conversions, which round to
+// nearest even.)
 template <int QT>
 __device__ __forceinline__ void split16(float a, float b, uint32_t &hi, uint32_t &lo) {
   if constexpr (QT == PA_BF16) {
-    const uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b);
-    hi = ha | (hb << 16);
-    lo = f32_to_bf16_rne(a - u2f(ha << 16)) | ((uint32_t)f32_to_bf16_rne(b - u2f(hb << 16)) << 16);
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = {(__bf16)a, (__bf16)b};
+    const h2 l = {(__bf16)(a - (float)h.x), (__bf16)(b - (float)h.y)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
   } else {
-    const uint32_t ha = f32_to_f16_rne(a), hb = f32_to_f16_rne(b);
-    hi = ha | (hb << 16);
-    lo = f32_to_f16_rne(a - f16_lo(ha)) | ((uint32_t)f32_to_f16_rne(b - f16_lo(hb)) << 16);
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = {(_Float16)a, (_Float16)b};
+    const h2 l = {(_Float16)(a - (float)h.x), (_Float16)(b - (float)h.y)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
   }
 }
 
