@@ -655,8 +655,8 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 
   // ---- per-wave softmax state ----------------------------------------------
   float m[4], l[4];
-  // P.V on MFMA for 4 to 16 query heads of a 128-wide head (16-bit queries,
-  // one block per unit): 16x16x16 products per 16 output columns replace the
+  // P.V on MFMA for 4 to 16 query heads of a 128-wide head (16-bit queries;
+  // per block of the unit): 16x16x16 products per 16 output columns replace the
   // GH x 8 fp32 FMAs per V element on the vector ALU (rows past GH repeat
   // the first GH, as in the logits tile).
   // Lane (r, c) of the V layout holds tokens 4i + r (i = 0..3), elements
@@ -666,7 +666,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   // and enter as two 16-bit parts (split16), V exactly.
   // Output rows are heads 4 (l / 16) + j, the rows this lane's softmax state
   // already holds, so the rescale needs no exchange.
-  constexpr bool PVM = GH >= 4 && D == 128 && QT != PA_F32 && NBI == 1;
+  constexpr bool PVM = GH >= 4 && D == 128 && QT != PA_F32;
   float acc[PVM ? 1 : GH][8];
   f32x4 acc2[PVM ? 8 : 1];
   auto reset = [&]() {
@@ -813,27 +813,29 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         acc2[t].z *= al[2];
         acc2[t].w *= al[3];
       }
+#pragma unroll
+      for (int bi = 0; bi < NBI; ++bi) {
       // A: P[head tl][tokens 4i + jq], i = 0..3
       float pk[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = sh.p[wave][4 * i + jq][tl % GH];
+      for (int i = 0; i < 4; ++i) pk[i] = sh.p[wave][bi * kBs + 4 * i + jq][tl % GH];
       uint32_t h0, l0, h1, l1;  // probabilities, high and low parts
       split16<QT>(pk[0], pk[1], h0, l0);
       split16<QT>(pk[2], pk[3], h1, l1);
       const u32x2 aop = {h0, h1}, aol = {l0, l1};
       // B: the lane's V pieces (tokens 4i + r), the appended row in place of
       // the cache's, masked tokens zero
-      const bool newblk = APP && app.blk == jb;
+      const bool newblk = APP && app.blk == jb + bi;
       const VPiece<KT> &vp = app.v;
       VPiece<KT> pcs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tk = 4 * i + r;
-        const uint32_t keep = jb * kBs + tk < tok_lim ? ~0u : 0u;
+        const uint32_t keep = (jb + bi) * kBs + tk < tok_lim ? ~0u : 0u;
         const uint32_t mk = (newblk && tk == app.t) ? ~0u : 0u;
 #pragma unroll
         for (int w = 0; w < 2 * ElemBytes<KT>::value; ++w)
-          pcs[i].w[w] = ((vp.w[w] & mk) | (st.v[0][i].w[w] & ~mk)) & keep;
+          pcs[i].w[w] = ((vp.w[w] & mk) | (st.v[bi][i].w[w] & ~mk)) & keep;
       }
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -858,6 +860,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         }
         acc2[t] = mfma16<QT>(aop, bop, acc2[t]);
         acc2[t] = mfma16<QT>(aol, bop, acc2[t]);
+      }
       }
     } else {
       {
