@@ -35,9 +35,12 @@
 //     the full dot product whatever the MFMA's internal k order;
 //   * online softmax: block max over the 16 token lanes with DPP, running max
 //     m and per-lane partial sums l, rescale alpha = exp2(m_old - m_new);
-//   * P.V on the vector ALU: lane (r, c) of a V load holds 8 elements
-//     [8c, 8c+8) of token row r; the probabilities reach that layout through
-//     a small per-wave LDS buffer; fp32 accumulators acc[head][8].
+//   * P.V: lane (r, c) of a V load holds 8 elements [8c, 8c+8) of token row
+//     r. With 16-bit queries, d = 128 and 4 to 16 heads per workgroup it runs
+//     on 16x16x16 MFMAs (see PVM below: the probabilities in two 16-bit parts,
+//     V exactly, fp32 accumulators); otherwise on the vector ALU, the
+//     probabilities reaching the V layout through a small per-wave LDS buffer,
+//     fp32 accumulators acc[head][8].
 // At the end of a range the waves' (m, l, acc) are merged in LDS, in fixed
 // wave order, and written as the output or as one split partial.
 //
