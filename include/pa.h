@@ -340,11 +340,12 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapp
  *   out[b, h, :] = softmax(scale * q[b, h] . K_b^T) V_b over all context_lens[b]
  *                  tokens of sequence b.
  *
- * It is computed in two passes of the balanced split: the prefix of each
- * group, with the members' query rows stacked as extra query heads of each
+ * It is computed in two passes: the prefix of each group, in the balanced
+ * split, with the members' query rows stacked as extra query heads of each
  * KV head (so a prefix block is read once for all members), and each
- * sequence's suffix past its group's prefix; then the pieces of both passes
- * are merged with their softmax statistics, as in pa_decode_reduce.
+ * sequence's suffix past its group's prefix, in a single pass; then the
+ * pieces of both passes are merged with their softmax statistics, as in
+ * pa_decode_reduce.
  *
  * Arguments as pa_decode (balanced split), plus
  *   group_members  [num_groups, group_size] int32, device: sequence ids.

@@ -485,8 +485,7 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
   probe.num_kv_heads = num_kv_heads;
   probe.num_q_heads = (int)hq_stacked;
   a.prefix_splits = pa::balanced_num_splits(probe);
-  probe.num_q_heads = num_q_heads;
-  a.suffix_splits = pa::balanced_num_splits(probe);
+  a.suffix_splits = 0;  // the suffix pass is a single pass: B x Hq partials
   const size_t need = shared_prefix_layout(nullptr, num_seqs, num_groups, group_size, num_q_heads,
                                            head_dim, max_blocks_per_seq, a.q_elem_bytes,
                                            a.prefix_splits, a.suffix_splits, nullptr);

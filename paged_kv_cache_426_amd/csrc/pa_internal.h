@@ -103,7 +103,8 @@ struct SharedPrefixLaunch {
   int num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   float scale, k_scale, v_scale;
   int q_dtype, kv_dtype, q_elem_bytes;
-  int prefix_splits, suffix_splits;  // balanced-split shares of the two passes
+  int prefix_splits;  // balanced-split shares of the prefix pass
+  int suffix_splits;  // 0: the suffix pass runs single-pass, one partial per (sequence, head)
   SharedPrefixWorkspace ws;
 };
 

@@ -12,7 +12,9 @@
 //   2. the balanced-split decode kernel over the groups' prefixes, with
 //      group_size times the query heads: each prefix block is read once for
 //      all members of its group;
-//   3. the same kernel over every sequence's suffix;
+//   3. the same kernel over every sequence's suffix, in a single pass (one
+//      partial per sequence and query head: a suffix is a few blocks, too
+//      short for the balanced split's preamble to pay off);
 //   4. merge_kernel: per sequence and query head, the pieces of both passes
 //      merged into the output.
 //
@@ -170,9 +172,8 @@ struct MergeParams {
   const float *a_out, *a_max, *a_sum;
   int a_cols, a_splits;
   const int32_t *prefix_ctx;
-  // suffix pass: per query head, columns of its balanced split over the sequences
+  // suffix pass: one partial per (sequence, query head), [B, Hq]
   const float *b_out, *b_max, *b_sum;
-  int b_cols, b_splits;
   const int32_t *suffix_lens;
   const int32_t *seq_slot;
   int num_seqs, num_groups, group_size, num_q_heads, gqa;
@@ -200,14 +201,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeParams 
   const int M = p.group_size;
   const int slot = p.seq_slot[b];
   const int g = slot >= 0 ? slot / M : 0;
-  int a_first, a_np, b_first, b_np;
+  int a_first, a_np;
   balanced_span(p.prefix_ctx, p.num_groups, g, p.a_splits, s_red, a_first, a_np);
-  balanced_span(p.suffix_lens, p.num_seqs, b, p.b_splits, s_red, b_first, b_np);
+  const int b_np = p.suffix_lens[b] > 0 ? 1 : 0;
   if (slot < 0) a_np = 0;
   if (h >= p.num_q_heads) return;
   const int hs = stacked_head(h, slot >= 0 ? slot % M : 0, M, p.gqa);
   const size_t a_base = (size_t)hs * p.a_cols + a_first;
-  const size_t b_base = (size_t)h * p.b_cols + b_first;
+  const size_t b_base = (size_t)b * p.num_q_heads + h;
   // Pieces (prefix ones first, then suffix ones) are read R at a time, every
   // load of a batch issued before any is used: a batch costs one memory
   // round trip. The running max rescales what is summed so far.
@@ -303,15 +304,19 @@ int launch_shared_prefix(const SharedPrefixLaunch &a, void *stream) {
   e = launch_decode(d, stream);
   if (e) return e;
 
-  // suffix pass: every sequence past its prefix
+  // suffix pass: every sequence past its prefix, one range each; its partial
+  // goes to column 0 of [B, Hq, 1] (a sequence with an empty suffix writes
+  // zeros to `out`, which the merge overwrites)
   DecodeLaunch f = d;
+  f.out = a.out;
   f.q = a.q;
   f.block_tables = a.ws.suffix_tables;
   f.context_lens = a.ws.suffix_lens;
   f.num_seqs = a.num_seqs;
   f.num_q_heads = a.num_q_heads;
-  f.num_splits = a.suffix_splits;
-  f.max_partitions = a.suffix_splits + a.num_seqs;
+  f.mode = kSplitSingle;
+  f.num_splits = 0;
+  f.max_partitions = 1;
   f.tmp_out = a.ws.b_out;
   f.max_logits = a.ws.b_max;
   f.exp_sums = a.ws.b_sum;
@@ -329,8 +334,6 @@ int launch_shared_prefix(const SharedPrefixLaunch &a, void *stream) {
   mp.b_out = a.ws.b_out;
   mp.b_max = a.ws.b_max;
   mp.b_sum = a.ws.b_sum;
-  mp.b_cols = f.max_partitions;
-  mp.b_splits = a.suffix_splits;
   mp.suffix_lens = a.ws.suffix_lens;
   mp.seq_slot = a.ws.seq_slot;
   mp.num_seqs = a.num_seqs;
