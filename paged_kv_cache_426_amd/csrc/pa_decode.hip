@@ -88,48 +88,35 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
   if (np == 1 && p.skip_single) return;
   const size_t base = (p.mode == kSplitBalanced) ? (size_t)h * p.max_partitions + first
                                                  : bh * p.max_partitions;
-  // Pieces are read R at a time, every load of a batch issued before any is
-  // used, so that a sequence of at most R pieces costs one memory round trip
-  // (the first batch is loaded whole and kept for the weighted sum).
-  constexpr int R = 8;
-  float mm[R], ll[R], tt[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u)
-    if (u < np) {
-      mm[u] = p.max_logits[base + u];
-      ll[u] = p.exp_sums[base + u];
-      tt[u] = p.tmp_out[(base + u) * D + d];
-    }
-  float M = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < R; ++u)
-    if (u < np) M = fmaxf(M, mm[u]);
-  for (int i0 = R; i0 < np; i0 += R) {
-    float mx[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) mx[u] = i0 + u < np ? p.max_logits[base + i0 + u] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < R; ++u) M = fmaxf(M, mx[u]);
-  }
-  // weights w_p = l_p exp(m_p - M), summed in piece order
-  float W = 0.0f, O = 0.0f;
+  // Pieces are merged in one pass, R at a time: every load of a batch is
+  // issued before any is used (a batch costs one memory round trip), and the
+  // running maximum rescales what is summed so far. Weights
+  // w_p = l_p exp(m_p - M) are summed in piece order.
+  constexpr int R = 16;
+  float M = -INFINITY, W = 0.0f, O = 0.0f;
   for (int i0 = 0; i0 < np; i0 += R) {
-    if (i0 > 0) {
+    float mm[R], ll[R], tt[R];
 #pragma unroll
-      for (int u = 0; u < R; ++u)
-        if (i0 + u < np) {
-          mm[u] = p.max_logits[base + i0 + u];
-          ll[u] = p.exp_sums[base + i0 + u];
-          tt[u] = p.tmp_out[(base + i0 + u) * D + d];
-        }
+    for (int u = 0; u < R; ++u) {
+      const bool ok = i0 + u < np;
+      mm[u] = ok ? p.max_logits[base + i0 + u] : -INFINITY;
+      ll[u] = ok ? p.exp_sums[base + i0 + u] : 0.0f;
+      tt[u] = ok ? p.tmp_out[(base + i0 + u) * D + d] : 0.0f;
     }
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < R; ++u) bm = fmaxf(bm, mm[u]);
+    const float rs = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - bm) * kLog2e);
+    W *= rs;
+    O *= rs;
 #pragma unroll
     for (int u = 0; u < R; ++u)
       if (i0 + u < np) {
-        const float w = ll[u] * __builtin_amdgcn_exp2f((mm[u] - M) * kLog2e);
+        const float w = ll[u] * __builtin_amdgcn_exp2f((mm[u] - bm) * kLog2e);
         W += w;
         O = fmaf(w, tt[u], O);
       }
+    M = bm;
   }
   store_elem<OT>(p.out, bh * D + d, O / W);
 }
