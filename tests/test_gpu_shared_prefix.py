@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _forked(groups, samples, prompt, private, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16",
-            bs=16, seed=0, loners=()):
+            bs=16, seed=0, loners=(), mbs=None):
     """Forked groups in a custom workload: each group's members share the
     prompt's whole blocks (their table rows start with the same physical
     ids), then hold private blocks; ``loners`` are extra sequences in no
@@ -28,7 +28,7 @@ def _forked(groups, samples, prompt, private, Hq, Hkv, d, q_dtype="bf16", kv_dty
             ctx.append(prompt + private[(g * samples + m) % len(private)])
     ctx += list(loners)
     wl = W.custom(ctx, Hq, Hkv, d, q_dtype=q_dtype, kv_dtype=kv_dtype, bs=bs, seed=seed,
-                  extra_blocks=3)
+                  extra_blocks=3, mbs=mbs)
     bt = wl.block_tables.copy()
     pb = prompt // bs
     for g in range(groups):
@@ -98,6 +98,17 @@ def test_edge_cases():
     pl[2] = 0                    # group 2 shares nothing
     pl[0] = pl[0] + 7            # not whole blocks: rounded down
     _check(wl, members, pl, "edge cases")
+
+
+@pytest.mark.parametrize("mbs,Hq,q_dtype", [(2048, 32, "bf16"), (2100, 32, "bf16"),
+                                             (None, 64, "f32")])
+def test_wide_inputs(mbs, Hq, q_dtype):
+    """Wide block tables (2048 and 2100 entries, mostly unused) and wide
+    query rows (64 f32 heads: 32 KiB per sequence) through the set-up
+    kernel's table shift and query stacking."""
+    wl, members, pl = _forked(2, 3, 160, [5, 90], Hq, 8, 128, q_dtype=q_dtype,
+                              kv_dtype=q_dtype, seed=Hq, mbs=mbs)
+    _check(wl, members, pl, f"mbs={mbs} Hq={Hq} {q_dtype}")
 
 
 @pytest.mark.parametrize("bs", [32, 64])
