@@ -43,10 +43,11 @@ DEFAULT_WORKLOAD = "llama3_8b_b32"
 DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn",
               "int8": "int8"}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3fn": 1, "int8": 1}
-# the decode kernel's sources (the traffic counters are tied to them)
-DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_426_amd", "csrc", f)
-               for f in ("pa_decode_kernel.h", "pa_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3_8b_b32_traffic.md")
+# the decode kernel's sources: the traffic counters of a summary are tied to
+# them, or to the files its `sources` field lists
+CSRC = os.path.join(ROOT, "paged_kv_cache_426_amd", "csrc")
+DECODE_SRCS = ("pa_decode_kernel.h", "pa_device.h")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse_args(argv=None):
@@ -160,29 +161,38 @@ def copy_bytes(wl):
 # traffic measured by rocprofv3 counters (committed summary)
 # ---------------------------------------------------------------------------
 
-def decode_source_hash():
+def decode_source_hash(files=DECODE_SRCS):
+    """First 16 hex digits of the sha256 of the named csrc files, in order."""
     h = hashlib.sha256()
-    for path in DECODE_SRCS:
-        with open(path, "rb") as f:
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload, partition_size):
-    """HBM bytes per decode-kernel launch from the committed rocprofv3 counter
-    summary, or None when there is none for this workload / partition size or
-    the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(workload, shared):
+    return os.path.join(PROFILES, f"pa_decode_{workload}{'_shared_mode' if shared else ''}"
+                                  "_traffic.md")
+
+
+def committed_traffic(workload, partition_size, shared=False):
+    """HBM bytes per timed launch (the decode kernel; for the shared-prefix call
+    its four kernels together) from the committed rocprofv3 counter summary of
+    this workload, or None when there is none for this workload / partition
+    size / mode or a source it names changed since the counters were taken."""
+    path = traffic_file(workload, shared)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
     try:
         if fields.get("workload") != workload or int(fields["partition_size"]) != partition_size:
             return None
-        if fields.get("decode_source_sha256") != decode_source_hash():
+        files = tuple(fields["sources"].split()) if "sources" in fields else DECODE_SRCS
+        if fields.get("decode_source_sha256") != decode_source_hash(files):
             return None
         return float(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+    except (KeyError, ValueError, OSError):
         return None
 
 
@@ -480,7 +490,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if shared else committed_traffic(wl.name, P),
+            "traffic": committed_traffic(wl.name, P, shared),
             "kernel": ("shared-prefix decode: prep, prefix-pass and suffix-pass decode kernels "
                        "and merge, timed together, against the distinct K/V bytes" if shared
                        else "decode_kernel" + (" (split partials)" if P else " (single pass)") +
