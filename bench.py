@@ -18,11 +18,18 @@ JSON line:
   value      KV tokens attended per second (sum of context lengths / step time)
   gbps       algorithmic HBM GB/s of the step (every attended K/V byte once,
              plus q, out and the block-table entries read)
-  roofline   the dominant kernel (the decode kernel) timed alone with HIP
-             events on the stream it is launched on: algorithmic bytes per
-             launch / average launch time, against 8 TB/s
+  roofline   the decode timed alone with HIP events on the stream it is
+             launched on -- for a split decode the launch pair (partials
+             kernel + merge kernel), with the partials kernel alone beside
+             it: algorithmic bytes per call / average call time, against
+             8 TB/s
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
              workload, on this host's cores (a reported baseline only)
+  per_config every workload (tiny fp32, Llama-shaped, MHA, shared-prefix CoW,
+             long-context fp8, and the same with an int8 cache) at its own
+             launch configuration: decode time, KV tokens/s, GB/s and
+             fraction of 8 TB/s, the slot write and block copies, and the
+             oracle timed on a sample of that workload
 """
 
 import argparse
@@ -73,6 +80,10 @@ def parse_args(argv=None):
                     help="decode through pa_decode_shared_prefix (workloads with groups of "
                          "sequences sharing a prefix): shared blocks are read once per group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the pass over every workload at its own launch configuration")
+    ap.add_argument("--cpu-seconds-per-config", type=float, default=4.0,
+                    help="wall-clock budget of the CPU oracle sample of each per-config entry")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -176,10 +187,12 @@ def traffic_file(workload, shared):
 
 
 def committed_traffic(workload, partition_size, shared=False):
-    """HBM bytes per timed launch (the decode kernel; for the shared-prefix call
-    its four kernels together) from the committed rocprofv3 counter summary of
-    this workload, or None when there is none for this workload / partition
-    size / mode or a source it names changed since the counters were taken."""
+    """HBM bytes per timed call (the decode: for a split the partials kernel
+    and the merge kernel together; for the shared-prefix call its four kernels
+    together) from the committed rocprofv3 counter summary of this workload,
+    or None when there is none for this workload / partition size / mode, when
+    it does not cover the whole call (field `scope`), or when a source it
+    names changed since the counters were taken."""
     path = traffic_file(workload, shared)
     if not os.path.exists(path):
         return None
@@ -187,6 +200,8 @@ def committed_traffic(workload, partition_size, shared=False):
     fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
     try:
         if fields.get("workload") != workload or int(fields["partition_size"]) != partition_size:
+            return None
+        if partition_size and not shared and fields.get("scope") != "partials+merge":
             return None
         files = tuple(fields["sources"].split()) if "sources" in fields else DECODE_SRCS
         if fields.get("decode_source_sha256") != decode_source_hash(files):
@@ -245,6 +260,222 @@ def cpu_baseline(wl, budget_s):
 # GPU timing
 # ---------------------------------------------------------------------------
 
+def avg_launch_s(fn, n, stream, warm=10):
+    """Average duration of fn(i) over n back-to-back launches: HIP events on
+    the stream the work runs on, around all n, divided by n (the time between
+    launches is included)."""
+    import torch
+
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n / 1e3
+
+
+def bracketed_median_s(fn, n, stream):
+    """Median of n launches each bracketed by its own pair of events (higher
+    than avg_launch_s by the events' own cost)."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return ms[len(ms) // 2] / 1e3
+
+
+class Prepared:
+    """A workload's device inputs: the cache state after the step's history
+    writes (fp8 fill, private tokens) in L layer caches sharing one block
+    table, plus the step's own inputs."""
+
+    def __init__(self, wl, dev, layers):
+        import torch
+
+        import paged_kv_cache_426_amd as pa
+        import workloads as W
+
+        t = lambda a: W.to_device(a, dev)  # noqa: E731
+        self.wl = wl
+        self.dev = dev
+        self.q = t(wl.q)
+        self.bt = t(wl.block_tables)
+        self.cl = t(wl.context_lens)
+        self.cow = t(wl.cow_pairs)
+        self.new_k = t(wl.new_key) if wl.new_key is not None else None
+        self.new_v = t(wl.new_value) if wl.new_value is not None else None
+        self.new_s = t(wl.new_slots) if wl.new_slots is not None else None
+        k0, v0 = t(wl.k_cache), t(wl.v_cache)
+        if wl.hist_slots is not None and len(wl.hist_slots):
+            pa.copy_blocks(k0, v0, self.cow)
+            pa.reshape_and_cache(t(wl.hist_key), t(wl.hist_value), k0, v0, t(wl.hist_slots),
+                                 wl.k_scale, wl.v_scale)
+        self.layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(layers - 1)]
+        self.out = torch.empty_like(self.q)
+        self.gm = self.pl = self.ws_sp = None
+        if wl.prefix_members is not None:
+            self.gm = t(wl.prefix_members)
+            self.pl = t(wl.prefix_lens)
+            self.ws_sp = torch.empty(pa.decode_shared_prefix_workspace_size(
+                wl.num_seqs, self.gm.shape[0], self.gm.shape[1], wl.num_q_heads, wl.head_dim,
+                wl.max_blocks_per_seq, self.q.dtype), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def workspace(self, P):
+        import torch
+
+        import paged_kv_cache_426_amd as pa
+
+        wl = self.wl
+        if not P:
+            return None
+        return torch.empty(pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
+                                                    wl.max_blocks_per_seq, wl.block_size, P),
+                           dtype=torch.uint8, device=self.dev)
+
+    def decode_fn(self, P, ws):
+        """pa_decode (for a split: the partials kernel and the merge kernel)."""
+        import paged_kv_cache_426_amd as pa
+
+        wl = self.wl
+
+        def fn(i):
+            kc, vc = self.layers[i % len(self.layers)]
+            pa.decode(self.q, kc, vc, self.bt, self.cl, scale=wl.scale, k_scale=wl.k_scale,
+                      v_scale=wl.v_scale, partition_size=P, out=self.out, workspace=ws)
+        return fn
+
+    def shared_fn(self):
+        import paged_kv_cache_426_amd as pa
+
+        wl = self.wl
+
+        def fn(i):
+            kc, vc = self.layers[i % len(self.layers)]
+            pa.decode_shared_prefix(self.q, kc, vc, self.bt, self.cl, self.gm, self.pl,
+                                    scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                                    out=self.out, workspace=self.ws_sp)
+        return fn
+
+    def partials_fn(self, P):
+        """The partials kernel alone (no merge), for a split P != 0."""
+        import torch
+
+        import paged_kv_cache_426_amd as pa
+
+        wl = self.wl
+        B, Hq, d = wl.num_seqs, wl.num_q_heads, wl.head_dim
+        if P > 0:
+            NP = pa.num_partitions(wl.max_blocks_per_seq, wl.block_size, P)
+            lead, arg = (B, Hq, NP), P
+        else:
+            S = pa.decode_balanced_splits(Hq, wl.num_kv_heads, d, self.q.dtype,
+                                          self.layers[0][0].dtype) if P == -1 else -P
+            lead, arg = (Hq, S + B), -S
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        tmp = torch.empty(lead + (d,), **f32)
+        mx = torch.empty(lead, **f32)
+        sm = torch.empty(lead, **f32)
+
+        def fn(i):
+            kc, vc = self.layers[i % len(self.layers)]
+            pa.decode_partials(self.q, kc, vc, self.bt, self.cl, arg, scale=wl.scale,
+                               k_scale=wl.k_scale, v_scale=wl.v_scale, tmp_out=tmp,
+                               max_logits=mx, exp_sums=sm)
+        return fn, arg
+
+
+def measure_config(wl, dev, args, stream, cpu_seconds):
+    """One workload at its own launch configuration: the decode launch pair
+    (partials + merge; a single-pass decode is one launch), the partials
+    kernel alone, the shared-prefix call where the workload has prefix
+    groups, the slot write and the block copies; each against its
+    algorithmic bytes, with the oracle timed on a sample beside it."""
+    import torch
+
+    layers = 2 if wl.kv_bytes_attended > (1 << 30) else args.layers
+    prep = Prepared(wl, dev, layers)
+    P = wl.partition_size
+    n = max(20, args.roofline_launches // 2)
+    ws = prep.workspace(P)
+    db = decode_bytes(wl)
+    alg = db["kv"] + db["q"] + db["out"] + db["tables"] + db["ctx_lens"]
+    tokens = wl.tokens_attended
+    pair_s = avg_launch_s(prep.decode_fn(P, ws), n, stream)
+    e = {
+        "workload": wl.name,
+        "batch": wl.num_seqs,
+        "heads": f"{wl.num_q_heads}/{wl.num_kv_heads}/{wl.head_dim}",
+        "dtypes": f"{wl.q_dtype}/{wl.kv_dtype}",
+        "partition_size": P,
+        "tokens_attended": tokens,
+        "algorithmic_bytes": alg,
+        "decode_us": pair_s * 1e6,
+        "decode_launches": "partials + merge" if P else "single pass",
+        "kv_tokens_per_s": tokens / pair_s,
+        "gbps": alg / pair_s / 1e9,
+        "frac": alg / pair_s / 1e9 / HBM_PEAK_GBPS,
+        "traffic": committed_traffic(wl.name, P),
+    }
+    if P:
+        fn, arg = prep.partials_fn(P)
+        ps = avg_launch_s(fn, n, stream)
+        e["partials_only_us"] = ps * 1e6
+        e["partials_only_frac"] = alg / ps / 1e9 / HBM_PEAK_GBPS
+    if "distinct_blocks" in wl.info:
+        ub = unique_kv_bytes(wl)
+        ualg = ub + db["q"] + db["out"] + db["tables"] + db["ctx_lens"]
+        e["unique_kv_bytes"] = ub
+        e["frac_of_unique_bytes"] = ualg / pair_s / 1e9 / HBM_PEAK_GBPS
+        if prep.gm is not None:
+            ss = avg_launch_s(prep.shared_fn(), n, stream)
+            e["shared_prefix"] = {
+                "us": ss * 1e6, "kv_tokens_per_s": tokens / ss,
+                "gbps_unique": ualg / ss / 1e9, "frac": ualg / ss / 1e9 / HBM_PEAK_GBPS,
+                "effective_gbps_logical": alg / ss / 1e9,
+                "traffic": committed_traffic(wl.name, P, shared=True),
+                "launches": "prep + prefix pass + suffix pass + merge"}
+    # a1: the slot write of the step's new tokens; a2: the copy-on-write copies
+    import paged_kv_cache_426_amd as pa
+    if prep.new_s is not None:
+        def wfn(i):
+            kc, vc = prep.layers[i % len(prep.layers)]
+            pa.reshape_and_cache(prep.new_k, prep.new_v, kc, vc, prep.new_s, wl.k_scale,
+                                 wl.v_scale)
+        wt = avg_launch_s(wfn, 200, stream)
+        e["slot_write"] = {"us": wt * 1e6, "tokens": int((wl.new_slots >= 0).sum()),
+                           "bytes": write_bytes(wl), "gbps": write_bytes(wl) / wt / 1e9}
+    if len(wl.cow_pairs):
+        def cfn(i):
+            kc, vc = prep.layers[i % len(prep.layers)]
+            pa.copy_blocks(kc, vc, prep.cow)
+        ct = avg_launch_s(cfn, 200, stream)
+        e["block_copy"] = {"us": ct * 1e6, "pairs": int(len(wl.cow_pairs)),
+                           "bytes": copy_bytes(wl), "gbps": copy_bytes(wl) / ct / 1e9,
+                           "note": "the copied blocks fit the last-level cache across repeats"}
+    del prep, ws
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        e["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
+        e["gpu_over_cpu"] = e["kv_tokens_per_s"] / e["cpu_baseline"]["value"]
+    return e
+
+
+PER_CONFIG = ("tiny_fp32_gqa2", "llama3_8b_b32", "mha_b32_ctx4096", "shared_prefix_cow_b64",
+              "long_ctx_fp8_b8", "long_ctx_int8_b8")
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -253,7 +484,6 @@ def main(argv=None):
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import paged_kv_cache_426_amd as pa
@@ -264,6 +494,7 @@ def main(argv=None):
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
 
     t0 = time.perf_counter()
     kw = {} if args.partition_size is None else {"partition_size": args.partition_size}
@@ -276,48 +507,22 @@ def main(argv=None):
     log(f"workload {wl.name}: B={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
         f"d={wl.head_dim} kv={wl.kv_dtype} P={P} tokens={wl.tokens_attended} "
         f"pool={wl.num_blocks} blocks (built in {time.perf_counter() - t0:.1f} s)")
-
-    # device inputs; the step's history writes (fp8 fill, private tokens) are
-    # applied once, before timing, to every layer cache
-    t = lambda a: W.to_device(a, dev)  # noqa: E731
-    q = t(wl.q)
-    bt = t(wl.block_tables)
-    cl = t(wl.context_lens)
-    cow = t(wl.cow_pairs)
-    new_k = t(wl.new_key) if wl.new_key is not None else None
-    new_v = t(wl.new_value) if wl.new_value is not None else None
-    new_s = t(wl.new_slots) if wl.new_slots is not None else None
-    k0, v0 = t(wl.k_cache), t(wl.v_cache)
-    if wl.hist_slots is not None and len(wl.hist_slots):
-        pa.copy_blocks(k0, v0, cow)
-        pa.reshape_and_cache(t(wl.hist_key), t(wl.hist_value), k0, v0, t(wl.hist_slots),
-                             wl.k_scale, wl.v_scale)
-    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.layers - 1)]
-    out = torch.empty_like(q)
-    MBS = wl.max_blocks_per_seq
-    NP = pa.num_partitions(MBS, wl.block_size, P) if P > 0 else 0
-    ws = None
-    if P:
-        ws = torch.empty(pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
-                                                  MBS, wl.block_size, P),
-                         dtype=torch.uint8, device=dev)
+    prep = Prepared(wl, dev, args.layers)
+    q, bt, cl, layers, out = prep.q, prep.bt, prep.cl, prep.layers, prep.out
+    new_k, new_v, new_s, cow = prep.new_k, prep.new_v, prep.new_s, prep.cow
+    ws = prep.workspace(P)
     has_cow = len(wl.cow_pairs) > 0
-    torch.cuda.synchronize()
 
     # With --fused-append the slot write rides in the decode launch
     # (decode_append), which needs every new token at its sequence's last
     # position.
     fused = new_s is not None and args.fused_append and new_token_is_last(wl)
     shared = args.shared_prefix
-    if shared:
-        if wl.prefix_members is None:
-            print(f"--shared-prefix: workload {wl.name} has no prefix groups", file=sys.stderr)
-            return 2
-        gm = t(wl.prefix_members)
-        pl = t(wl.prefix_lens)
-        ws_sp = torch.empty(pa.decode_shared_prefix_workspace_size(
-            wl.num_seqs, gm.shape[0], gm.shape[1], wl.num_q_heads, wl.head_dim, wl.max_blocks_per_seq,
-            q.dtype), dtype=torch.uint8, device=dev)
+    if shared and prep.gm is None:
+        print(f"--shared-prefix: workload {wl.name} has no prefix groups", file=sys.stderr)
+        return 2
+
+    shared_call = prep.shared_fn() if shared else None
 
     def step(i):
         kc, vc = layers[i % len(layers)]
@@ -331,9 +536,7 @@ def main(argv=None):
         if new_s is not None:
             pa.reshape_and_cache(new_k, new_v, kc, vc, new_s, wl.k_scale, wl.v_scale)
         if shared:
-            pa.decode_shared_prefix(q, kc, vc, bt, cl, gm, pl, scale=wl.scale,
-                                    k_scale=wl.k_scale, v_scale=wl.v_scale, out=out,
-                                    workspace=ws_sp)
+            shared_call(i)
             return
         pa.decode(q, kc, vc, bt, cl, scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
                   partition_size=P, out=out, workspace=ws)
@@ -342,10 +545,8 @@ def main(argv=None):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
     w0 = time.perf_counter()
     for i in range(args.steps):
@@ -357,69 +558,25 @@ def main(argv=None):
     log(f"{args.steps} steps: {ms_per_step * 1e3:.2f} us/step on events, "
         f"{wall / args.steps * 1e6:.2f} us/step wall-clock")
 
-    # --- the dominant kernel alone, on its stream ----------------------------
-    # Its average launch duration is the elapsed time of HIP events recorded
-    # around n back-to-back launches, divided by n (the time between launches
-    # is included). Events bracketing each launch are recorded as well: their
-    # median is reported beside it, and is higher by the events' own cost.
+    # --- the dominant work alone, on its stream ------------------------------
+    # The decode as one launch pair: for a split, the partials kernel and the
+    # merge kernel (pa_decode enqueues both); the partials kernel alone is
+    # reported beside it.
     n_launch = args.roofline_launches
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
-    if P > 0:
-        nbh = wl.num_seqs * wl.num_q_heads * NP
-        flat = ws.view(torch.float32)
-        tmp_out = flat[: nbh * wl.head_dim].view(wl.num_seqs, wl.num_q_heads, NP, wl.head_dim)
-        max_logits = flat[nbh * wl.head_dim: nbh * (wl.head_dim + 1)].view(
-            wl.num_seqs, wl.num_q_heads, NP)
-        exp_sums = flat[nbh * (wl.head_dim + 1): nbh * (wl.head_dim + 2)].view(
-            wl.num_seqs, wl.num_q_heads, NP)
-        split_arg = P
-    elif P < 0:
-        # the balanced split's partial kernel alone, with the share count the
-        # automatic choice resolves to
-        S = pa.decode_balanced_splits(wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                      q.dtype, layers[0][0].dtype) if P == -1 else -P
-        npc = S + wl.num_seqs
-        tmp_out = torch.empty((wl.num_q_heads, npc, wl.head_dim), dtype=torch.float32, device=dev)
-        max_logits = torch.empty((wl.num_q_heads, npc), dtype=torch.float32, device=dev)
-        exp_sums = torch.empty((wl.num_q_heads, npc), dtype=torch.float32, device=dev)
-        split_arg = -S
-        log(f"balanced split: {S} shares")
     if shared:
-        def kernel(i):
-            kc, vc = layers[i % len(layers)]
-            pa.decode_shared_prefix(q, kc, vc, bt, cl, gm, pl, scale=wl.scale,
-                                    k_scale=wl.k_scale, v_scale=wl.v_scale, out=out,
-                                    workspace=ws_sp)
-    elif P:
-        def kernel(i):
-            kc, vc = layers[i % len(layers)]
-            pa.decode_partials(q, kc, vc, bt, cl, split_arg, scale=wl.scale, k_scale=wl.k_scale,
-                               v_scale=wl.v_scale, tmp_out=tmp_out, max_logits=max_logits,
-                               exp_sums=exp_sums)
+        kernel = prep.shared_fn()
     else:
-        def kernel(i):
-            kc, vc = layers[i % len(layers)]
-            pa.decode(q, kc, vc, bt, cl, scale=wl.scale, k_scale=wl.k_scale,
-                      v_scale=wl.v_scale, partition_size=0, out=out)
-    for i in range(10):
-        kernel(i)
-    torch.cuda.synchronize()
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for i in range(n_launch):
-        kernel(i)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    kern_avg_s = r0.elapsed_time(r1) / n_launch / 1e3
-    for i in range(n_launch):
-        starts[i].record(stream)
-        kernel(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kern_med_s = sorted(kern_ms)[len(kern_ms) // 2] / 1e3
+        kernel = prep.decode_fn(P, ws)
+    kern_avg_s = avg_launch_s(kernel, n_launch, stream)
+    kern_med_s = bracketed_median_s(kernel, n_launch, stream)
+    part_avg_s = None
+    if P and not shared:
+        pfn, split_arg = prep.partials_fn(P)
+        part_avg_s = avg_launch_s(pfn, n_launch, stream)
+        if P < 0:
+            log(f"balanced split: {-split_arg} shares")
+    log(f"decode: {kern_avg_s * 1e6:.2f} us per call" +
+        (f" (partials alone {part_avg_s * 1e6:.2f} us)" if part_avg_s else ""))
 
     # --- optional copy calibration for counter scaling ----------------------
     if args.copy_calibration:
@@ -433,9 +590,7 @@ def main(argv=None):
 
     # --- bytes and the JSON line ---------------------------------------------
     db = decode_bytes(wl)
-    kernel_alg = db["kv"] + db["q"] + db["tables"] + db["ctx_lens"]
-    if not P:
-        kernel_alg += db["out"]
+    kernel_alg = db["kv"] + db["q"] + db["out"] + db["tables"] + db["ctx_lens"]
     step_alg = db["total"] + (append_bytes(wl) if fused else write_bytes(wl)) + copy_bytes(wl)
     if shared:
         # every distinct K/V row once: shared blocks are read once per group
@@ -445,6 +600,32 @@ def main(argv=None):
     tokens = wl.tokens_attended
     step_s = ms_per_step / 1e3
     achieved = kernel_alg / kern_avg_s / 1e9
+    if shared:
+        kname = ("shared-prefix decode: prep, prefix-pass and suffix-pass decode kernels and "
+                 "merge, timed together, against the distinct K/V bytes")
+    elif P:
+        kname = "decode launch pair: decode_kernel (split partials) + reduce_kernel (merge)"
+    else:
+        kname = "decode_kernel (single pass)"
+    roof = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBPS,
+        "traffic": committed_traffic(wl.name, P, shared),
+        "kernel": kname + ("; the step runs its variant with the slot write fused"
+                           if fused else ""),
+        "kernel_avg_us": kern_avg_s * 1e6,
+        "kernel_timing": f"HIP events around {n_launch} back-to-back calls",
+        "kernel_bracketed_median_us": kern_med_s * 1e6,
+        "algorithmic_bytes_per_launch": kernel_alg,
+        "bytes_per_unit": db["kv_per_token"],
+        "units_per_launch": (unique_kv_bytes(wl) // db["kv_per_token"]) if shared else tokens,
+    }
+    if part_avg_s:
+        roof["partials_only_us"] = part_avg_s * 1e6
+        roof["partials_only_frac"] = kernel_alg / part_avg_s / 1e9 / HBM_PEAK_GBPS
     result = {
         "metric": "paged decode: KV tokens attended/s and achieved HBM GB/s (% of peak), 1 GPU",
         "value": tokens / step_s,
@@ -484,37 +665,35 @@ def main(argv=None):
         "gbps": step_alg / step_s / 1e9,
         "hbm_frac": step_alg / step_s / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_alg,
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": committed_traffic(wl.name, P, shared),
-            "kernel": ("shared-prefix decode: prep, prefix-pass and suffix-pass decode kernels "
-                       "and merge, timed together, against the distinct K/V bytes" if shared
-                       else "decode_kernel" + (" (split partials)" if P else " (single pass)") +
-                       ("; the step runs its variant with the slot write fused"
-                        if fused else "")),
-            "kernel_avg_us": kern_avg_s * 1e6,
-            "kernel_timing": f"HIP events around {n_launch} back-to-back launches",
-            "kernel_bracketed_median_us": kern_med_s * 1e6,
-            "algorithmic_bytes_per_launch": kernel_alg,
-            "bytes_per_unit": db["kv_per_token"],
-            "units_per_launch": (unique_kv_bytes(wl) // db["kv_per_token"]) if shared else tokens,
-        },
+        "roofline": roof,
     }
     if "distinct_blocks" in wl.info:
         ub = unique_kv_bytes(wl)
         result["unique_kv_bytes"] = ub
         result["unique_kv_gbps_kernel"] = ub / kern_avg_s / 1e9
         result["shared_ratio"] = wl.info.get("shared_ratio")
+    del prep, ws, layers, out, q
+    torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+
+    # --- every workload at its own launch configuration ----------------------
+    if not args.no_per_config and args.block_size is None and args.placement is None \
+            and args.partition_size is None:
+        per = []
+        for name in PER_CONFIG:
+            t1 = time.perf_counter()
+            w = wl if name == wl.name else W.build(name)
+            e = measure_config(w, dev, args, stream,
+                               0.0 if args.no_cpu_baseline else args.cpu_seconds_per_config)
+            log(f"per-config {name}: decode {e['decode_us']:.2f} us, {e['frac'] * 100:.1f} % of "
+                f"8 TB/s ({time.perf_counter() - t1:.1f} s)")
+            per.append(e)
+        result["per_config"] = per
     print(json.dumps(result), flush=True)
     return 0
 

@@ -170,7 +170,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
  *   block_tables  [num_seqs, max_blocks_per_seq] int32; only the first
  *                 ceil(n / block_size) entries of row b are read.
  *   context_lens  [num_seqs] int32, each in [0, max_blocks_per_seq*block_size].
- *   scale         softmax scale, normally 1/sqrt(head_dim).
+ *   scale         softmax scale. A NaN selects the attention formula's
+ *                 1/sqrt(d_k): the float32 nearest to 1/sqrt(head_dim). An
+ *                 infinite scale gives PA_ERR_BAD_SHAPE. (The same holds for
+ *                 every decode entry point below.)
  *   partition_size see "Context splitting" above. A split decode runs the
  *                 partial kernel into `workspace` (a sequence that falls in
  *                 one piece is written to `out` directly), then the merge

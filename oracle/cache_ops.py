@@ -31,6 +31,14 @@ def _encode_rows(rows: np.ndarray, cache_dtype, scale) -> np.ndarray:
     float32 division (numpy's float32 divide is IEEE)."""
     if rows.dtype == cache_dtype:
         return rows.copy()
+    if cache_dtype in (np.uint8, np.int8) and rows.dtype in (np.uint16, np.float16):
+        # a 16-bit source has 65536 bit patterns: the same encoding evaluated
+        # once per pattern, then looked up per element
+        patterns = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(rows.dtype)
+        with np.errstate(over="ignore", invalid="ignore"):  # inf and NaN patterns
+            codes = _encode_rows(patterns.astype(np.float32) if rows.dtype == np.float16
+                                 else to_f32_exact(patterns), cache_dtype, scale)
+        return codes[np.asarray(rows).view(np.uint16)]
     if cache_dtype in (np.uint8, np.int8):
         x32 = to_f32_exact(rows)
         q = x32 / np.float32(scale)
@@ -59,7 +67,7 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
 
 
 def reshape_and_cache_bulk(key, value, k_cache, v_cache, slot_mapping,
-                           k_scale=1.0, v_scale=1.0):
+                           k_scale=1.0, v_scale=1.0, chunk=8192):
     """Same result as ``reshape_and_cache`` for many tokens at once.
 
     The per-token loop is replaced by one indexed assignment over the flat
@@ -72,8 +80,13 @@ def reshape_and_cache_bulk(key, value, k_cache, v_cache, slot_mapping,
     assert len(np.unique(slots[live])) == len(live), "duplicate slots in one call"
     kf = k_cache.reshape(k_cache.shape[0] * bs, *k_cache.shape[2:])
     vf = v_cache.reshape(v_cache.shape[0] * bs, *v_cache.shape[2:])
-    kf[slots[live]] = _encode_rows(np.asarray(key)[live], k_cache.dtype, k_scale)
-    vf[slots[live]] = _encode_rows(np.asarray(value)[live], v_cache.dtype, v_scale)
+    key, value = np.asarray(key), np.asarray(value)
+    # tokens in chunks, so that the float64 temporaries of an 8-bit encoding
+    # stay small for long histories (the encoding is elementwise)
+    for c in range(0, len(live), chunk):
+        t = live[c:c + chunk]
+        kf[slots[t]] = _encode_rows(key[t], k_cache.dtype, k_scale)
+        vf[slots[t]] = _encode_rows(value[t], v_cache.dtype, v_scale)
     return k_cache, v_cache
 
 

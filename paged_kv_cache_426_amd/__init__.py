@@ -10,7 +10,6 @@ a GPU, or without the built library, raises.
 """
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -146,6 +145,12 @@ def _i64(t: torch.Tensor, name: str) -> None:
         raise PaError(f"{name} must be int64")
 
 
+def _scale_arg(scale: Optional[float]) -> float:
+    """The softmax scale as passed to the C ABI: None becomes a NaN, which the
+    library resolves to its default 1/sqrt(head_dim)."""
+    return float("nan") if scale is None else float(scale)
+
+
 def num_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
     return lib().pa_num_partitions(max_blocks_per_seq, block_size, partition_size)
 
@@ -187,8 +192,6 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
     if checks.debug_checks_enabled():
         checks.check_decode(block_tables, context_lens, NB, bs)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
@@ -198,7 +201,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                           _ptr(context_lens), B, Hq, Hkv, d, bs, NB, MBS, float(scale),
+                           _ptr(context_lens), B, Hq, Hkv, d, bs, NB, MBS, _scale_arg(scale),
                            dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
                            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
     return out
@@ -235,8 +238,6 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     if checks.debug_checks_enabled():
         checks.check_shared_prefix(block_tables, context_lens, group_members, prefix_lens, bs)
     G, M = group_members.shape
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
@@ -247,7 +248,7 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().pa_decode_shared_prefix(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-        _ptr(group_members), _ptr(prefix_lens), B, G, M, Hq, Hkv, d, bs, NB, MBS, float(scale),
+        _ptr(group_members), _ptr(prefix_lens), B, G, M, Hq, Hkv, d, bs, NB, MBS, _scale_arg(scale),
         dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale), _ptr(workspace),
         ws_bytes, _stream(dev)))
     return out
@@ -269,8 +270,8 @@ def decode_append(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     if key.shape != (B, Hkv, d) or value.shape != key.shape or key.dtype != q.dtype or \
             value.dtype != q.dtype:
         raise PaError("key and value must be [B, Hkv, d] in q's type")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
+    if checks.debug_checks_enabled():
+        checks.check_append(block_tables, context_lens, bs)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:
@@ -282,7 +283,7 @@ def decode_append(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     _check(lib().pa_decode_append(_ptr(out), _ptr(q), _ptr(key.contiguous()),
                                   _ptr(value.contiguous()), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs, NB,
-                                  MBS, float(scale), dtype_code(q), dtype_code(k_cache),
+                                  MBS, _scale_arg(scale), dtype_code(q), dtype_code(k_cache),
                                   float(k_scale), float(v_scale), int(partition_size),
                                   _ptr(workspace), ws_bytes, _stream(dev)))
     return out
@@ -301,8 +302,6 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, partition_s
     B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
     if checks.debug_checks_enabled():
         checks.check_decode(block_tables, context_lens, NB, bs)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     lead = (B, Hq) if partition_size > 0 else (Hq,)
     if tmp_out is None:
         NP = num_partitions(MBS, bs, partition_size) if partition_size > 0 \
@@ -320,7 +319,7 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, partition_s
     _check(lib().pa_decode_partials(_ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
                                     tmp_out.shape[n], _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs,
-                                    NB, MBS, float(scale), dtype_code(q), dtype_code(k_cache),
+                                    NB, MBS, _scale_arg(scale), dtype_code(q), dtype_code(k_cache),
                                     float(k_scale), float(v_scale), int(partition_size),
                                     _stream(dev)))
     return tmp_out, max_logits, exp_sums

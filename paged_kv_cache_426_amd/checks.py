@@ -23,6 +23,10 @@ The contracts (include/pa.h states each beside its entry point):
 * block copy: every id in [0, num_blocks); destinations distinct and never a
   source of the same call (copy-on-write copies a shared block to a fresh
   one: "PagedAttention deep dive" section 2.3);
+* decode with append: the slot of each non-empty sequence's last position
+  (n - 1) is distinct, and the block holding it is private to that sequence
+  (no other sequence's used block-table entries name it), since the launch
+  writes that row while other workgroups read their own blocks;
 * shared-prefix decode: members in [-1, num_seqs), each sequence in at most
   one slot; each group's whole-block prefix lies within every member's
   context and its table entries are the same physical blocks for every
@@ -35,7 +39,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["ContractError", "set_debug_checks", "debug_checks_enabled", "check_decode",
-           "check_slot_mapping", "check_block_mapping", "check_shared_prefix"]
+           "check_slot_mapping", "check_block_mapping", "check_shared_prefix", "check_append"]
 
 
 class ContractError(ValueError):
@@ -146,3 +150,27 @@ def check_shared_prefix(block_tables, context_lens, group_members, prefix_lens,
                 j = int(np.nonzero(bt[b, :pb] != bt[ids[0], :pb])[0][0])
                 raise ContractError(f"group {g}: sequences {ids[0]} and {b} hold different "
                                     f"blocks at prefix block {j}")
+
+
+def check_append(block_tables, context_lens, block_size: int) -> None:
+    """Decode with append writes each non-empty sequence's position n - 1 in
+    the same launch that reads the caches: the block holding it must be named
+    by no other sequence's used table entries (a shared block is copied first,
+    "PagedAttention deep dive" section 2.3), which also makes the written
+    slots distinct."""
+    bt = _host(block_tables).astype(np.int64)
+    cl = _host(context_lens).astype(np.int64)
+    B = bt.shape[0]
+    used = -(-cl // block_size)
+    owners = {}
+    for b in range(B):
+        for blk in np.unique(bt[b, : used[b]]).tolist():
+            owners.setdefault(int(blk), set()).add(b)
+    for b in range(B):
+        if cl[b] <= 0:
+            continue
+        last = int(bt[b, (cl[b] - 1) // block_size])
+        others = sorted(owners.get(last, set()) - {b})
+        if others:
+            raise ContractError(f"sequence {b} appends into block {last}, which sequence "
+                                f"{others[0]} also reads (copy the shared block first)")

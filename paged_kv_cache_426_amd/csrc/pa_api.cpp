@@ -28,6 +28,13 @@ bool supported_decode_pair(int q, int kv) {
 
 pa_status status_of(int hip_err) { return hip_err == 0 ? PA_OK : PA_ERR_LAUNCH; }
 
+// The softmax scale: a NaN selects 1/sqrt(d_k) of the attention formula
+// ("KV-Cache evolution", section 1), the float32 nearest to 1/sqrt(head_dim)
+// (evaluated in double, rounded once).
+float resolve_scale(float scale, int head_dim) {
+  return isnan(scale) ? (float)(1.0 / sqrt((double)head_dim)) : scale;
+}
+
 // Shared checks of pa_decode and pa_decode_partials.
 pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
@@ -45,7 +52,7 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
     return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
   if (partition_size < 0 && num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
-  if (!isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (isinf(scale)) return PA_ERR_BAD_SHAPE;  // NaN: the default scale
   if (quantised(kv_dtype) && (!isfinite(k_scale) || !isfinite(v_scale)))
     return PA_ERR_BAD_SHAPE;
   // int8 decode kernels are built for 16-token blocks only
@@ -151,7 +158,7 @@ pa_status pa_decode_partials(float *tmp_out, float *max_logits, float *exp_sums,
   a.head_dim = head_dim;
   a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.scale = scale;
+  a.scale = resolve_scale(scale, head_dim);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.q_dtype = q_dtype;
@@ -232,7 +239,7 @@ pa_status decode_impl(void *out, const void *q, const void *new_k, const void *n
   a.head_dim = head_dim;
   a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.scale = scale;
+  a.scale = resolve_scale(scale, head_dim);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.q_dtype = q_dtype;
@@ -472,7 +479,7 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
   a.head_dim = head_dim;
   a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.scale = scale;
+  a.scale = resolve_scale(scale, head_dim);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.q_dtype = q_dtype;

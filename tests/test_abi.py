@@ -94,7 +94,8 @@ def _decode(**kw):
     (dict(P=-1, ws=FAKE, wsb=10), 4),
     (dict(P=-1, B=1025), 3),                       # balanced split: at most 1024 sequences
     (dict(P=-4096), 3),                            # at most 2048 shares
-    (dict(scale=float("nan")), 2),
+    (dict(scale=float("inf")), 2),                 # NaN selects the default; inf is refused
+    (dict(scale=float("-inf")), 2),
     (dict(qt=pa.PA_BF16, kt=pa.PA_FP8_E4M3FN, ks=float("inf")), 2),
     (dict(Hq=65536 * 8, Hkv=65536), 3),            # launch grid limit
 ])
@@ -104,6 +105,7 @@ def test_decode_validation(kw, status):
 
 def test_zero_sequences_is_a_no_op():
     assert _decode(B=0) == 0
+    assert _decode(B=0, scale=float("nan")) == 0   # the default scale passes validation
 
 
 def _append(**kw):

@@ -31,9 +31,11 @@ def test_committed_summaries_parse():
             assert os.path.exists(os.path.join(bench.CSRC, name)), name
 
 
-def _write(dirpath, workload, shared, P, sha, sources=None):
+def _write(dirpath, workload, shared, P, sha, sources=None, scope="partials+merge"):
     lines = [f"- workload: `{workload}`", f"- partition_size: `{P}`",
              f"- decode_source_sha256: `{sha}`", "- traffic_bytes_per_launch: `12345`"]
+    if scope:
+        lines.append(f"- scope: `{scope}`")
     if sources:
         lines.append(f"- sources: `{sources}`")
     name = f"pa_decode_{workload}{'_shared_mode' if shared else ''}_traffic.md"
@@ -55,3 +57,8 @@ def test_traffic_is_tied_to_workload_mode_and_sources(tmp_path, monkeypatch):
     # a summary whose hash covers fewer files than it names is stale
     _write(tmp_path, "wl_d", False, -1, bench.decode_source_hash(), srcs)
     assert bench.committed_traffic("wl_d", -1) is None
+    # a split decode's figure must cover the partials kernel and the merge
+    _write(tmp_path, "wl_e", False, -1, bench.decode_source_hash(), scope=None)
+    assert bench.committed_traffic("wl_e", -1) is None
+    _write(tmp_path, "wl_e", False, 0, bench.decode_source_hash(), scope=None)
+    assert bench.committed_traffic("wl_e", 0) == 12345.0         # single pass: one kernel

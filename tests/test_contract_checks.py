@@ -72,6 +72,25 @@ def test_shared_prefix_breaches():
         checks.check_shared_prefix(bt, cl, np.array([[0, 3]], np.int32), np.array([16], np.int32), 16)
 
 
+def test_append_breaches():
+    """Decode with append: the block holding each sequence's last position is
+    private to it. A shared prefix block is fine while nobody appends into it;
+    appending into a block another sequence reads (or two sequences appending
+    into one block) is refused."""
+    bt = np.array([[5, 6, 7, 0], [5, 6, 8, 0], [5, 9, 3, 0]], dtype=np.int32)
+    checks.check_append(bt, np.array([40, 40, 33], np.int32), 16)   # last blocks 7, 8, 3
+    checks.check_append(bt, np.array([40, 0, 33], np.int32), 16)    # empty sequence: no write
+    with pytest.raises(ContractError, match="block 6"):
+        checks.check_append(bt, np.array([32, 40, 33], np.int32), 16)  # 0 appends into shared 6
+    with pytest.raises(ContractError, match="block 5"):
+        checks.check_append(bt, np.array([40, 40, 16], np.int32), 16)  # 2 appends into shared 5
+    same = np.array([[4, 0], [4, 0]], dtype=np.int32)
+    with pytest.raises(ContractError, match="block 4"):
+        checks.check_append(same, np.array([3, 5], np.int32), 16)      # two writers, one block
+    wl = W.build("tiny_fp32_gqa2")
+    checks.check_append(wl.block_tables, wl.context_lens, wl.block_size)
+
+
 def test_binding_runs_the_checks_when_enabled(monkeypatch):
     """With debug checks on, a binding call with a breach raises before the
     library is reached (CPU tensors would be refused later anyway)."""
@@ -90,6 +109,11 @@ def test_binding_runs_the_checks_when_enabled(monkeypatch):
             pa.copy_blocks(kc, kc, torch.tensor([[1, 2], [3, 2]], dtype=torch.int64))
         with pytest.raises(ContractError):
             pa.reshape_and_cache(q[:, :2], q[:, :2], kc, kc, torch.tensor([1, 1]))
+        shared = torch.from_numpy(wl.block_tables.copy())
+        shared[1, : shared.shape[1]] = shared[0]       # both sequences in sequence 0's blocks
+        new = torch.from_numpy(wl.new_key)
+        with pytest.raises(ContractError, match="appends into block"):
+            pa.decode_append(q, new, new, kc, kc, shared, cl)
     finally:
         pa.set_debug_checks(False)
     assert not checks.debug_checks_enabled()

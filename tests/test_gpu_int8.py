@@ -127,17 +127,16 @@ def test_int8_large_blocks_are_refused():
 
 def test_long_ctx_int8_b8():
     """The long-context batch with an int8 cache, at the benchmark's launch
-    configuration (512-token partitions) and the balanced split, on the
-    shortest and the longest sequence."""
+    configuration (512-token partitions) and the balanced split: every
+    sequence's output and the whole pool after the writes."""
     wl = W.build("long_ctx_int8_b8")
-    seqs = [int(np.argmin(wl.context_lens)), int(np.argmax(wl.context_lens))]
-    kc, vc, ref = oracle_step(wl, seqs=seqs)
+    print("[int8] long_ctx_int8_b8: oracle", flush=True)
+    kc, vc, ref = oracle_step(wl)
+    assert not np.isnan(ref).any()
     for P in (wl.partition_size, -1):
         print(f"[int8] long_ctx_int8_b8 P={P}", flush=True)
         d, out = device_step(wl, P)
         torch.cuda.synchronize()
-        blocks = np.unique(np.concatenate([
-            wl.block_tables[b, : -(-int(wl.context_lens[b]) // wl.block_size)] for b in seqs]))
-        assert np.array_equal(W.to_numpy(d["k_cache"])[blocks], kc[blocks])
-        assert np.array_equal(W.to_numpy(d["v_cache"])[blocks], vc[blocks])
+        assert np.array_equal(W.to_numpy(d["k_cache"]), kc)
+        assert np.array_equal(W.to_numpy(d["v_cache"]), vc)
         assert_close(W.widen_to_f64(out), ref, wl.q_dtype, f"long_ctx_int8_b8 P={P}")

@@ -330,3 +330,45 @@ def test_sampled_subset_matches_full():
     assert np.array_equal(part[1, [0, 3]], full[1, [0, 3]])
     assert np.isnan(part[0]).all()
     assert to_f64(wl.q).shape == (3, 4, 16)
+
+
+@pytest.mark.parametrize("bs", [32, 64, 256])
+def test_pieces_in_16_token_units_on_large_blocks(bs):
+    """``paged_decode_pieces(unit=16)`` on a cache of bs-token blocks: the
+    bounds of each piece count 16-token sub-blocks, whatever the block size.
+    Checked by brute force over each piece's own token slice, and against the
+    same pieces on the cache's 16-token view (a block of bs tokens is bs/16
+    consecutive 16-token blocks); a piece list read in bs-token units (the
+    plausible slip) gives different statistics."""
+    rng = np.random.default_rng(bs)
+    ctx = [1, 47, 0, 200, 129, 64]
+    q, K, V, kc, vc, table, cl = _random_case(rng, ctx, 4, 2, 8, bs)
+    pieces = balanced_pieces(ctx, 16, 5)
+    m, l, o = paged_decode_pieces(q, kc, vc, table, cl, 0.3, pieces, unit=16)
+    sc32 = float(np.float32(0.3))
+    for i, (s, b, fb, eb) in enumerate(pieces):
+        lo, hi = 16 * fb, min(16 * eb, ctx[b])
+        assert lo < hi
+        for h in range(4):
+            sc = [sc32 * float(np.dot(q[b, h], K[b][j, h // 2])) for j in range(lo, hi)]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            assert m[i, h] == pytest.approx(mx, abs=1e-12)
+            assert l[i, h] == pytest.approx(sum(e), abs=1e-12)
+            ref = sum(ei * V[b][lo + j, h // 2] for j, ei in enumerate(e)) / sum(e)
+            np.testing.assert_allclose(o[i, h], ref, rtol=0, atol=1e-12)
+    # the 16-token view of the same pool and tables
+    k = bs // 16
+    kc16 = kc.reshape(kc.shape[0] * k, 16, *kc.shape[2:])
+    vc16 = vc.reshape(vc.shape[0] * k, 16, *vc.shape[2:])
+    t16 = (table.astype(np.int64)[:, :, None] * k + np.arange(k)).reshape(len(ctx), -1)
+    m2, l2, o2 = paged_decode_pieces(q, kc16, vc16, t16, cl, 0.3, pieces)
+    assert np.array_equal(m, m2) and np.array_equal(l, l2) and np.array_equal(o, o2)
+    np.testing.assert_allclose(reduce_pieces(m, l, o, pieces, len(ctx)),
+                               paged_decode(q, kc, vc, table, cl, 0.3), rtol=0, atol=1e-12)
+    # bounds read in bs-token units instead select other tokens (or none)
+    try:
+        m3, _, _ = paged_decode_pieces(q, kc, vc, table, cl, 0.3, pieces)
+    except ValueError:  # an empty slice
+        return
+    assert not np.allclose(m3, m)

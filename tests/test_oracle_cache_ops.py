@@ -142,3 +142,36 @@ def test_copy_on_write_end_to_end():
     assert np.array_equal(kc[6, 2], new_k[0])                   # a's own token
     slot_b, cow_b = pool.append_slot(b)      # b is now the only holder: in place
     assert cow_b is None and slot_b == 0 * bs + 2
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+@pytest.mark.parametrize("cache,scale", [("fp8", 0.013), ("fp8", 1.0), ("int8", 0.021),
+                                         ("int8", 3.5e-5)])
+def test_slot_write_16bit_patterns_match_direct_encoding(src, cache, scale):
+    """The 8-bit slot write of a 16-bit source looks each bit pattern's code
+    up in a table of all 65536 patterns: over every pattern (NaN, infinities,
+    subnormals, both zeros included) it equals the encoding applied to
+    float32(x) / float32(scale) element by element, and the chunked bulk
+    write equals the per-token loop."""
+    from oracle import int8_encode
+    from oracle.cache_ops import _encode_rows
+
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if src == "bf16":
+        rows, x32 = pats, (pats.astype(np.uint32) << 16).view(np.float32)
+    else:
+        rows = pats.view(np.float16)
+        x32 = rows.astype(np.float32)
+    cdt = np.uint8 if cache == "fp8" else np.int8
+    enc = e4m3fn_encode if cache == "fp8" else int8_encode
+    with np.errstate(invalid="ignore", over="ignore"):
+        want = enc(x32 / np.float32(scale))
+    assert np.array_equal(_encode_rows(rows.reshape(256, 1, 256), cdt, scale).reshape(-1), want)
+    # bulk (chunked) against the loop on a 16-bit source
+    rng = np.random.default_rng(7)
+    key = rows[rng.integers(0, 1 << 16, size=(37, 2, 8))]
+    kc = np.zeros((12, 4, 2, 8), cdt)
+    slots = rng.permutation(48)[:37]
+    a = reshape_and_cache(key, key, kc.copy(), kc.copy(), slots, scale, scale)
+    b = reshape_and_cache_bulk(key, key, kc.copy(), kc.copy(), slots, scale, scale, chunk=5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
