@@ -27,8 +27,10 @@
  *     owned by the caller. The library borrows it for the work it enqueues
  *     and keeps no reference afterwards; the caller keeps it alive until the
  *     stream has passed that work. The library allocates no memory and is
- *     reentrant; its only process-wide data is a cache of device properties
- *     (compute-unit count, kernel occupancy) behind a mutex.
+ *     reentrant; its process-wide data is a cache of device properties
+ *     (compute-unit count, kernel occupancy) behind a mutex, and the fixed
+ *     per-device scratch array of pa_decode_noalloc (the one entry point
+ *     whose overlapping calls on a device race, see there).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default
  *     stream. All work is enqueued asynchronously on it.
  *   - Cache layout: k_cache and v_cache are [num_blocks, block_size,
@@ -69,7 +71,8 @@ typedef enum pa_status {
                                 /* sizes are inconsistent (Hq % Hkv != 0, ...)        */
   PA_ERR_UNSUPPORTED = 3,       /* valid but not built: head_dim, block_size, dtypes  */
   PA_ERR_WORKSPACE_TOO_SMALL = 4,
-  PA_ERR_LAUNCH = 5             /* the HIP runtime refused a kernel launch            */
+  PA_ERR_LAUNCH = 5,            /* the HIP runtime refused a kernel launch            */
+  PA_ERR_SCRATCH_LIMIT = 6      /* pa_decode_noalloc: partials exceed its scratch     */
 } pa_status;
 
 /* Element types. fp8_e4m3fn is OCP E4M3FN (bias 7, max 448, no infinities).
@@ -190,6 +193,37 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                     float scale, int q_dtype, int kv_dtype, float k_scale, float v_scale,
                     int partition_size, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, result and errors as pa_decode. A split decode
+ * (partition_size != 0) keeps its partials in a fixed device array inside
+ * the library, pa_decode_noalloc_scratch_bytes() bytes (16 MiB) per device,
+ * held until the process ends; no memory is allocated per call. A split
+ * whose partials exceed it returns PA_ERR_SCRATCH_LIMIT without enqueuing
+ * anything (the partials need pa_decode_workspace_size(...) bytes, with the
+ * share count resolved: num_q_heads * (S + num_seqs) * (head_dim + 2) * 4
+ * for the balanced split, e.g. 1.6 MB for 32 sequences, 32 query heads,
+ * head_dim 128 and 64 shares). The array is shared by every call on a
+ * device: calls that overlap on one device (different streams or host
+ * threads without ordering between them) race on it; calls ordered on one
+ * stream do not. Nothing in it needs clearing between calls (every partial
+ * is written before it is read). The first split call on a device looks up
+ * the array's address (hipGetSymbolAddress); a failure there returns
+ * PA_ERR_LAUNCH.
+ */
+pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                            int q_dtype, int kv_dtype, float k_scale, float v_scale,
+                            int partition_size, void *stream);
+
+/* Bytes of the fixed per-device scratch pa_decode_noalloc uses. */
+size_t pa_decode_noalloc_scratch_bytes(void);
 
 /*
  * pa_decode_append -- one decode step with the new token appended.

@@ -22,7 +22,7 @@ __all__ = [
     "ContractError", "set_debug_checks",
     "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN", "PA_INT8",
     "PaError", "lib", "library_path", "dtype_code",
-    "decode", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
+    "decode", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
     "decode_shared_prefix", "decode_shared_prefix_workspace_size",
     "num_partitions", "decode_balanced_splits", "reshape_and_cache", "copy_blocks",
     "PARTITION_AUTO",
@@ -78,6 +78,11 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_workspace_size.argtypes = [i32] * 6
         L.pa_decode.restype = i32
         L.pa_decode.argtypes = [vp] * 6 + [i32] * 7 + [f32, i32, i32, f32, f32, i32, vp, sz, vp]
+        L.pa_decode_noalloc.restype = i32
+        L.pa_decode_noalloc.argtypes = ([vp] * 6 + [i32] * 7 +
+                                        [f32, i32, i32, f32, f32, i32, vp])
+        L.pa_decode_noalloc_scratch_bytes.restype = sz
+        L.pa_decode_noalloc_scratch_bytes.argtypes = []
         L.pa_decode_append.restype = i32
         L.pa_decode_append.argtypes = ([vp] * 8 + [i32] * 7 +
                                        [f32, i32, i32, f32, f32, i32, vp, sz, vp])
@@ -205,6 +210,34 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
                            int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
     return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                   partition_size: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode() with the split partials in the library's fixed per-device
+    scratch instead of a workspace (C: pa_decode_noalloc). Pass ``out`` to
+    allocate nothing at all. Calls that overlap on one GPU race on the
+    scratch."""
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, out)
+    B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PaError("out must match q in shape and type")
+    _check(lib().pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs,
+                                   NB, MBS, _scale_arg(scale), dtype_code(q),
+                                   dtype_code(k_cache), float(k_scale), float(v_scale),
+                                   int(partition_size), _stream(dev)))
+    return out
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return lib().pa_decode_noalloc_scratch_bytes()
 
 
 def decode_shared_prefix_workspace_size(num_seqs: int, num_groups: int, group_size: int,

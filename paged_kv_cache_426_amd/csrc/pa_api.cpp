@@ -82,6 +82,9 @@ const char *pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "configuration not supported by this build";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_SCRATCH_LIMIT:
+      return "split partials exceed the fixed scratch of pa_decode_noalloc "
+             "(pa_decode_noalloc_scratch_bytes); use pa_decode with a workspace";
   }
   return "unknown status";
 }
@@ -312,6 +315,33 @@ pa_status pa_decode(void *out, const void *q, const void *k_cache, const void *v
                      max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
                      partition_size, workspace, workspace_bytes, stream);
 }
+
+pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                            int q_dtype, int kv_dtype, float k_scale, float v_scale,
+                            int partition_size, void *stream) {
+  if (!out) return PA_ERR_NULL_POINTER;
+  pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                              max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                              partition_size);
+  if (st != PA_OK) return st;
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  if (partition_size != 0 && num_seqs > 0) {
+    if (pa::noalloc_scratch(&ws) != 0) return PA_ERR_LAUNCH;
+    ws_bytes = pa::kNoallocScratchBytes;
+  }
+  st = decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
+                   num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                   partition_size, ws, ws_bytes, stream);
+  return st == PA_ERR_WORKSPACE_TOO_SMALL ? PA_ERR_SCRATCH_LIMIT : st;
+}
+
+size_t pa_decode_noalloc_scratch_bytes(void) { return pa::kNoallocScratchBytes; }
 
 pa_status pa_decode_append(void *out, const void *q, const void *key, const void *value,
                            void *k_cache, void *v_cache, const int32_t *block_tables,

@@ -272,4 +272,41 @@ int launch_reduce(const ReduceLaunch &a, void *stream) {
   return (int)hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// fixed device scratch of pa_decode_noalloc
+// ---------------------------------------------------------------------------
+
+// The split partials of pa_decode_noalloc live here instead of in a caller's
+// workspace. Each device the library runs on holds its own copy for the life
+// of the process. In host code `scratch` is only a stand-in for the device
+// variable: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+int noalloc_scratch(void **ptr) {
+  static std::mutex mu;
+  static std::map<int, void *> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return (int)e;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *ptr = it->second;
+    return 0;
+  }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+  }
+  addr[dev] = p;
+  *ptr = p;
+  return 0;
+}
+
 }  // namespace pa

@@ -115,6 +115,13 @@ int launch_shared_prefix(const SharedPrefixLaunch &a, void *stream);
 // fill every compute unit once at the decode kernel's occupancy.
 int balanced_num_splits(const DecodeLaunch &a);
 
+// Size of the fixed device scratch that pa_decode_noalloc uses for split
+// partials, and its address on the current device (looked up with
+// hipGetSymbolAddress on the first call per device). Returns 0 or the
+// runtime's error code.
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+int noalloc_scratch(void **ptr);
+
 // Block sizes the decode kernels take: 16 << k tokens, k = 0 .. kMaxSubLog2
 // (16 to 256). Returns k, or -1 for any other size.
 constexpr int kMaxSubLog2 = 4;
