@@ -223,7 +223,7 @@ def cpu_baseline(wl, budget_s):
 
     import oracle
 
-    kc, vc = wl.k_cache, wl.v_cache
+    kc, vc = wl.k_cache.copy(), wl.v_cache.copy()  # the workload's own arrays stay as built
     done_tokens, done_seqs, t_used = 0, 0, 0.0
     order = [int(b) for b in np.random.default_rng(0).permutation(wl.num_seqs)]
     while t_used < budget_s:
@@ -404,7 +404,7 @@ def measure_config(wl, dev, args, stream, cpu_seconds):
     algorithmic bytes, with the oracle timed on a sample beside it."""
     import torch
 
-    layers = 2 if wl.kv_bytes_attended > (1 << 30) else args.layers
+    layers = 2 if wl.kv_bytes_attended() > (1 << 30) else args.layers
     prep = Prepared(wl, dev, layers)
     P = wl.partition_size
     n = max(20, args.roofline_launches // 2)
