@@ -121,27 +121,27 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
   store_elem<OT>(p.out, bh * D + d, O / W);
 }
 
-KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, bool balanced,
+KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, int kind,
                             bool append, bool large) {
   if (q_dtype == PA_F32 && kv_dtype == PA_F32)
-    return large ? decode_kernels_f32_f32_large(d, gh, balanced, append)
-                 : decode_kernels_f32_f32(d, gh, balanced, append);
+    return large ? decode_kernels_f32_f32_large(d, gh, kind, append)
+                 : decode_kernels_f32_f32(d, gh, kind, append);
   if (q_dtype == PA_F16 && kv_dtype == PA_F16)
-    return large ? decode_kernels_f16_f16_large(d, gh, balanced, append)
-                 : decode_kernels_f16_f16(d, gh, balanced, append);
+    return large ? decode_kernels_f16_f16_large(d, gh, kind, append)
+                 : decode_kernels_f16_f16(d, gh, kind, append);
   if (q_dtype == PA_BF16 && kv_dtype == PA_BF16)
-    return large ? decode_kernels_bf16_bf16_large(d, gh, balanced, append)
-                 : decode_kernels_bf16_bf16(d, gh, balanced, append);
+    return large ? decode_kernels_bf16_bf16_large(d, gh, kind, append)
+                 : decode_kernels_bf16_bf16(d, gh, kind, append);
   if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN)
-    return large ? decode_kernels_f16_fp8_large(d, gh, balanced, append)
-                 : decode_kernels_f16_fp8(d, gh, balanced, append);
+    return large ? decode_kernels_f16_fp8_large(d, gh, kind, append)
+                 : decode_kernels_f16_fp8(d, gh, kind, append);
   if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN)
-    return large ? decode_kernels_bf16_fp8_large(d, gh, balanced, append)
-                 : decode_kernels_bf16_fp8(d, gh, balanced, append);
+    return large ? decode_kernels_bf16_fp8_large(d, gh, kind, append)
+                 : decode_kernels_bf16_fp8(d, gh, kind, append);
   if (q_dtype == PA_F16 && kv_dtype == PA_INT8 && !large)
-    return decode_kernels_f16_int8(d, gh, balanced, append);
+    return decode_kernels_f16_int8(d, gh, kind, append);
   if (q_dtype == PA_BF16 && kv_dtype == PA_INT8 && !large)
-    return decode_kernels_bf16_int8(d, gh, balanced, append);
+    return decode_kernels_bf16_int8(d, gh, kind, append);
   return {nullptr, 0};
 }
 
@@ -173,16 +173,37 @@ int fill_workgroups(const void *fn, int threads) {
   return n;
 }
 
+// The balanced-split kernel of a launch: one wave per head row where the
+// head rows fill whole eight-wave workgroups and that kernel is built,
+// otherwise shares dealt to all waves of a workgroup.
+struct BalancedChoice {
+  KernelRef k;
+  bool row_waves;
+  int rowgroups;  // grid.y: workgroups per share
+};
+
+BalancedChoice balanced_kernel(const DecodeLaunch &a, bool append, bool large) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int gh = heads_per_workgroup(group);
+  const long long rows = (long long)a.num_kv_heads * (group / gh);
+  if (rows % 8 == 0) {
+    const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRowWaves,
+                                          append, large);
+    if (k.fn) return {k, true, (int)(rows / 8)};
+  }
+  return {decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindShares, append, large),
+          false, (int)rows};
+}
+
 int balanced_num_splits(const DecodeLaunch &a) {
-  const int gh = heads_per_workgroup(a.num_q_heads / a.num_kv_heads);
-  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, true, false,
-                                        false);
-  if (!k.fn) return 2;
-  const int cus = fill_workgroups(k.fn, k.threads);
+  const BalancedChoice c = balanced_kernel(a, false, false);
+  if (!c.k.fn) return 2;
+  const int cus = fill_workgroups(c.k.fn, c.k.threads);
   if (cus <= 0) return kMaxAutoSplits / 8;
-  const long long groups = (long long)a.num_kv_heads * (a.num_q_heads / a.num_kv_heads / gh);
-  // two shares per workgroup, as many workgroups as fit at once
-  long long s = 2 * (((long long)cus + groups - 1) / groups);
+  // row waves: one share per workgroup; otherwise two shares per workgroup;
+  // as many workgroups as fit at once
+  const long long per = ((long long)cus + c.rowgroups - 1) / c.rowgroups;
+  long long s = c.row_waves ? per : 2 * per;
   if (s < 2) s = 2;
   if (s > kMaxAutoSplits) s = kMaxAutoSplits;
   return (int)s;
@@ -225,14 +246,22 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.k_scale = a.k_scale;
   p.v_scale_w = a.v_scale;
   const int gh = heads_per_workgroup(p.group);
-  const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, wide,
-                                        a.new_k != nullptr, p.sub_log2 > 0);
-  if (!k.fn) return (int)hipErrorInvalidValue;
+  const bool append = a.new_k != nullptr;
+  const bool large = p.sub_log2 > 0;
   const int head_groups = a.num_kv_heads * (p.group / gh);
+  KernelRef k;
   dim3 grid;
-  if (wide) grid = dim3((p.num_splits + 1) / 2, head_groups, 1);
-  else if (a.mode == kSplitFixed) grid = dim3(a.max_partitions, head_groups, a.num_seqs);
-  else grid = dim3(1, head_groups, a.num_seqs);
+  if (wide) {
+    const BalancedChoice c = balanced_kernel(a, append, large);
+    k = c.k;
+    grid = c.row_waves ? dim3(p.num_splits, c.rowgroups, 1)
+                       : dim3((p.num_splits + 1) / 2, head_groups, 1);
+  } else {
+    k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRanges, append, large);
+    grid = a.mode == kSplitFixed ? dim3(a.max_partitions, head_groups, a.num_seqs)
+                                 : dim3(1, head_groups, a.num_seqs);
+  }
+  if (!k.fn) return (int)hipErrorInvalidValue;
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(k.fn, grid, dim3(k.threads), args, 0,
                                  static_cast<hipStream_t>(stream));

@@ -4,8 +4,8 @@
 
 namespace pa {
 
-KernelRef decode_kernels_bf16_bf16_large(int d, int gh, bool balanced, bool append) {
-  return by_d<PA_BF16, PA_BF16, true>(d, gh, balanced, append);
+KernelRef decode_kernels_bf16_bf16_large(int d, int gh, int kind, bool append) {
+  return by_d<PA_BF16, PA_BF16, true>(d, gh, kind, append);
 }
 
 }  // namespace pa

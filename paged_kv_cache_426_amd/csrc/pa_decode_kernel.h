@@ -372,6 +372,7 @@ struct Shared {
   int ctx[kMaxBalancedSeqs];        // balanced split: context length of each sequence
   int wave_sum[NW];
   int first[2];  // balanced split: the sequence holding the first block of each share taken
+  int progress[NW];  // one wave per head row: units computed by each wave
 };
 
 // The appended token of a segment's sequence (decode with append): the raw
@@ -509,7 +510,7 @@ struct Seg {
 // first unit of the next segment is already being loaded (its block ids and
 // query fragments were fetched one segment ahead), so a switch between
 // ranges costs only the epilogue of the finished range.
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB>
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB, bool RW>
 __device__ __forceinline__ void run_ranges(const DecodeParams &p,
                                            Shared<QT, KT, D, GH, NBI, NW> &sh, const Item (&items)[2],
                                            int n_items, int b_first, int n_first, int blo_first,
@@ -525,6 +526,10 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = uniform(tid >> 6);
+  // waves that share a range's units: all NW, or (RW: one wave per head
+  // row) the wave alone; dw is this wave's place among them
+  constexpr int ND = RW ? 1 : NW;
+  const int dw = RW ? 0 : wave;
   const int jq = lane >> 4;  // MFMA lane group
   const int tl = lane & 15;  // MFMA column: token within a block
   const int r = lane / G::lpt;  // V layout: token row within a load
@@ -549,10 +554,10 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     sg.piece = piece;
     sg.whole = whole;
     sg.u0 = u0;
-    sg.w0 = (wave - u0 % NW + NW) % NW;
+    sg.w0 = (dw - u0 % ND + ND) % ND;
     sg.c = ch;
     const int nunits = (bhi - blo + NBI - 1) / NBI;
-    sg.nk = sg.w0 < nunits ? (nunits - sg.w0 + NW - 1) / NW : 0;
+    sg.nk = sg.w0 < nunits ? (nunits - sg.w0 + ND - 1) / ND : 0;
     const int nchunks = max(1, (sg.nk + kIdsUnits - 1) / kIdsUnits);
     sg.kn = max(0, min(kIdsUnits, sg.nk - ch * kIdsUnits));
     sg.last = ch == nchunks - 1;
@@ -601,7 +606,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   // within that physical block
   auto fetch_ids = [&](const Seg &sg) {
     const int kk = sg.c * kIdsUnits + lane / NBI;
-    const int j = sg.blo + (sg.w0 + kk * NW) * NBI + lane % NBI;
+    const int j = sg.blo + (sg.w0 + kk * ND) * NBI + lane % NBI;
     const bool ok = sg.valid && kk < sg.nk && j < sg.bhi;
     const int32_t *row = p.block_tables + (size_t)(sg.valid ? sg.b : 0) * p.max_blocks_per_seq;
     const int e = ok ? j : 0;
@@ -909,9 +914,94 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     wave_lds_fence();
   };
 
+  // One wave per head row: the two waves of a SIMD have the same work, but
+  // the hardware issues for the older one first, which then finishes far
+  // ahead (about 30 against 44 us on the Llama-shaped batch) and leaves its
+  // SIMD half idle. A wave that is ahead of its SIMD partner (wave ^ 4)
+  // drops its issue priority, one behind raises it. Only the issue order
+  // changes, never the arithmetic.
+  int done_units = 0;
+  if (RW && lane == 0) sh.progress[wave] = 0;
+  auto pace = [&]() {
+    if constexpr (RW && NW == 8) {
+      ++done_units;
+      if (lane == 0) sh.progress[wave] = done_units;
+      const int other = sh.progress[wave ^ 4];
+      if (done_units > other) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(2);
+    }
+  };
+
+  // end of a range with one wave per head row (RW): the wave alone holds the
+  // range's softmax state and writes its heads' partial (or the output, for
+  // a whole sequence) with no exchange between waves
+  auto epilogue_wave = [&](int b, int piece, bool whole, int h0) {
+  #pragma unroll
+    for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
+    const bool to_out = whole && p.direct;
+    auto put = [&](int h, int d0, const float (&x)[8], float M, float L) {
+      const size_t bh = (size_t)b * Hq + h0 + h;
+      const float inv = p.v_scale / L;
+      if (to_out) {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) store_elem<QT>(p.out, bh * D + d0 + e, x[e] * inv);
+      } else {
+        const size_t pi = (size_t)(h0 + h) * p.max_partitions + piece;
+        float *dst = p.tmp_out + pi * D + d0;
+        *reinterpret_cast<f32x4 *>(dst) =
+            f32x4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
+        *reinterpret_cast<f32x4 *>(dst + 4) =
+            f32x4{x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv};
+        if (d0 == 0) {
+          p.max_logits[pi] = M * kLn2;
+          p.exp_sums[pi] = L;
+        }
+      }
+    };
+    if constexpr (PVM) {
+      // lane (tl, jq): heads 4 jq + v, elements 8 tl + t (rows past GH
+      // repeat the first GH and are not written)
+      if (4 * jq < GH) {
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x[8];
+  #pragma unroll
+          for (int t = 0; t < 8; ++t)
+            x[t] = v == 0 ? acc2[t].x : v == 1 ? acc2[t].y : v == 2 ? acc2[t].z : acc2[t].w;
+          put(4 * jq + v, 8 * tl, x, m[v], l[v]);
+        }
+      }
+    } else {
+      if (4 * jq < GH && tl == 0) {
+  #pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (v < GH) {
+            sh.m[wave][4 * jq + v] = m[v];
+            sh.l[wave][4 * jq + v] = l[v];
+          }
+      }
+  #pragma unroll
+      for (int h = 0; h < GH; ++h)
+  #pragma unroll
+        for (int e = 0; e < 8; ++e)
+  #pragma unroll
+          for (int off = G::lpt; off < kWave; off <<= 1) acc[h][e] += __shfl_xor(acc[h][e], off);
+      wave_lds_fence();
+      if (r == 0) {
+  #pragma unroll
+        for (int h = 0; h < GH; ++h) put(h, 8 * c, acc[h], sh.m[wave][h], sh.l[wave][h]);
+      }
+      wave_lds_fence();
+    }
+  };
+
   // end of a range: merge the waves' softmax states and write the range's
   // partial (or the output, for a whole sequence)
   auto epilogue = [&](int b, int piece, bool whole, int h0) {
+    if constexpr (RW) {
+      epilogue_wave(b, piece, whole, h0);
+      return;
+    }
     // merge the waves: sums over the token lanes / rows, then across waves
   #pragma unroll
     for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
@@ -1023,15 +1113,17 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     const int g_cur = cur.g, g_nxt = nxt.valid ? nxt.g : cur.g;
     // the first head row of a KV head writes the appended token back
     const bool writer = appending && cur.h0 % p.group == 0;
-    const int jb0 = cur.blo + (cur.w0 + cur.c * kIdsUnits * NW) * NBI;
+    const int jb0 = cur.blo + (cur.w0 + cur.c * kIdsUnits * ND) * NBI;
     const int tok_lim = min(cur.bhi * kBs, cur.n);
     for (int k = 0; k < kpad - NS; k += NS) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int u = k + s + NS - 1;
         issue(ids_cur, u, u < kn, g_cur, st[(s + NS - 1) % NS]);
-        if (k + s < kn)
-          compute_unit(jb0 + (k + s) * NW * NBI, tok_lim, q_cur, st[s], app, g_cur, writer);
+        if (k + s < kn) {
+          compute_unit(jb0 + (k + s) * ND * NBI, tok_lim, q_cur, st[s], app, g_cur, writer);
+          pace();
+        }
       }
     }
     // the last step, peeled: it issues this segment's last unit and the
@@ -1043,8 +1135,10 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       for (int s = 0; s < NS; ++s) {
         if (s == 0) issue(ids_cur, kpad - 1, kpad - 1 < kn, g_cur, st[NS - 1]);
         else issue(ids_nxt, s - 1, nxt.valid && s - 1 < nxt.kn, g_nxt, st[s - 1]);
-        if (k + s < kn)
-          compute_unit(jb0 + (k + s) * NW * NBI, tok_lim, q_cur, st[s], app, g_cur, writer);
+        if (k + s < kn) {
+          compute_unit(jb0 + (k + s) * ND * NBI, tok_lim, q_cur, st[s], app, g_cur, writer);
+          pace();
+        }
       }
     }
     // move to the next segment (copies of loads issued a segment ago, made
@@ -1066,9 +1160,10 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     ids_nxt = fetch_ids(nxt);
     load_q(nxt.valid ? nxt.b : cur.b, nxt.valid ? nxt.h0 : cur.h0, q_nxt);
   }
+
 }
 
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB>
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB, bool RW>
 __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
   __shared__ Shared<QT, KT, D, GH, NBI, NW> sh;
   const int tid = threadIdx.x;
@@ -1135,9 +1230,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       // the first blocks of this workgroup's shares (see below), and the
       // sequences holding them: each thread checks its own sequences
       const int S = min(p.num_splits, all);
-      const int s0 = 2 * blockIdx.x;
+      const int s0 = RW ? blockIdx.x : 2 * blockIdx.x;
       const long long f0 = s0 < S ? (long long)s0 * all / S : -1;
-      const long long f1 = s0 + 1 < S ? (long long)(s0 + 1) * all / S : -1;
+      const long long f1 = !RW && s0 + 1 < S ? (long long)(s0 + 1) * all / S : -1;
       int ex = base + incl - tot;
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
@@ -1158,6 +1253,19 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
     // two). The cache rows of neighbouring KV heads sit in different halves
     // of the memory interleave, which the hardware serves at different
     // rates; pairing gives every workgroup the same mix.
+    if constexpr (RW) {
+      // One wave per head row: workgroup (x, y) reads share x of head rows
+      // NW y .. NW y + NW - 1, wave w taking row NW y + w, so every
+      // workgroup reads whole cache blocks (all of their KV heads) and has
+      // the same mix of heads.
+      const int s = blockIdx.x;
+      const int h0 = (blockIdx.y * NW + uniform(tid >> 6)) * GH;
+      if (s >= S) return;
+      items[0] = Item{h0, h0 / p.group, s, (int)((long long)s * total / S),
+                      (int)((long long)(s + 1) * total / S)};
+      items[1] = items[0];
+      n_items = 1;
+    } else {
     const int y = blockIdx.y;
     const int y2 = (y ^ 1) < (int)gridDim.y ? (y ^ 1) : y;
     const int s0 = 2 * blockIdx.x;
@@ -1170,6 +1278,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
       items[k] = Item{h0, h0 / p.group, s, (int)((long long)s * total / S),
                       (int)((long long)(s + 1) * total / S)};
     }
+    }
     first_b = uniform(sh.first[0]);
     const int st = uniform(sh.start[first_b]), en = uniform(sh.start[first_b + 1]);
     first_n = uniform(sh.ctx[first_b]);
@@ -1178,7 +1287,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
     first_piece = items[0].share + first_b;
     first_whole = first_lo == 0 && first_hi == en - st;
   }
-  run_ranges<QT, KT, D, GH, NBI, NS, NW, APP, SUB>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
+  run_ranges<QT, KT, D, GH, NBI, NS, NW, APP, SUB, RW>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
                                      first_piece, first_whole);
 }
 
@@ -1207,63 +1316,73 @@ constexpr int balanced_waves() {
 }
 
 // SUB: blocks larger than 16 tokens (read as 16-token sub-blocks); the
-// 16-token kernels leave the sub-block arithmetic out.
+// 16-token kernels leave the sub-block arithmetic out. kind is a KernelKind:
+// ranges (single pass or fixed partitions), balanced shares dealt to all
+// waves of a workgroup, or balanced shares with one wave per head row (built
+// where eight waves fit the registers; {nullptr, 0} otherwise).
 template <int QT, int KT, int D, int GH, bool APP, bool SUB>
-KernelRef kernel_of(bool balanced) {
+KernelRef kernel_of(int kind) {
   constexpr int NBI = units_of<QT, KT, GH>();
   constexpr int NWB = balanced_waves<QT, KT, D, GH, APP>();
-  if (balanced)
+  if (kind == kKindRowWaves) {
+    if constexpr (NWB == 8)
+      return {reinterpret_cast<const void *>(
+                  &decode_kernel<QT, KT, D, GH, NBI, kStages, 8, APP, SUB, true>),
+              8 * kWave};
+    return {nullptr, 0};
+  }
+  if (kind == kKindShares)
     return {reinterpret_cast<const void *>(
-                &decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP, SUB>),
+                &decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP, SUB, false>),
             NWB * kWave};
   return {reinterpret_cast<const void *>(
-              &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP, SUB>),
+              &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP, SUB, false>),
           kFixedWaves * kWave};
 }
 
 template <int QT, int KT, int D, int GH, bool SUB>
-KernelRef with_append(bool balanced, bool append) {
-  return append ? kernel_of<QT, KT, D, GH, true, SUB>(balanced)
-                : kernel_of<QT, KT, D, GH, false, SUB>(balanced);
+KernelRef with_append(int kind, bool append) {
+  return append ? kernel_of<QT, KT, D, GH, true, SUB>(kind)
+                : kernel_of<QT, KT, D, GH, false, SUB>(kind);
 }
 
 template <int QT, int KT, int D, bool SUB>
-KernelRef by_gh(int gh, bool balanced, bool append) {
+KernelRef by_gh(int gh, int kind, bool append) {
   switch (gh) {
-    case 1: return with_append<QT, KT, D, 1, SUB>(balanced, append);
-    case 2: return with_append<QT, KT, D, 2, SUB>(balanced, append);
-    case 4: return with_append<QT, KT, D, 4, SUB>(balanced, append);
-    case 8: return with_append<QT, KT, D, 8, SUB>(balanced, append);
-    case 16: return with_append<QT, KT, D, 16, SUB>(balanced, append);
+    case 1: return with_append<QT, KT, D, 1, SUB>(kind, append);
+    case 2: return with_append<QT, KT, D, 2, SUB>(kind, append);
+    case 4: return with_append<QT, KT, D, 4, SUB>(kind, append);
+    case 8: return with_append<QT, KT, D, 8, SUB>(kind, append);
+    case 16: return with_append<QT, KT, D, 16, SUB>(kind, append);
   }
   return {nullptr, 0};
 }
 
 template <int QT, int KT, bool SUB>
-KernelRef by_d(int d, int gh, bool balanced, bool append) {
+KernelRef by_d(int d, int gh, int kind, bool append) {
   switch (d) {
-    case 64: return by_gh<QT, KT, 64, SUB>(gh, balanced, append);
-    case 128: return by_gh<QT, KT, 128, SUB>(gh, balanced, append);
+    case 64: return by_gh<QT, KT, 64, SUB>(gh, kind, append);
+    case 128: return by_gh<QT, KT, 128, SUB>(gh, kind, append);
   }
   return {nullptr, 0};
 }
 }  // namespace
 
 // The kernels of one element-type pair: the decode kernel for head size d,
-// gh query heads per workgroup, the balanced split or not, with append or
-// not; {nullptr, 0} when not built. Each pair has one translation unit for
+// gh query heads per workgroup, a KernelKind, with append or not;
+// {nullptr, 0} when not built. Each pair has one translation unit for
 // 16-token blocks and one (_large) for larger blocks.
-KernelRef decode_kernels_f32_f32(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_f16_f16(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_bf16_bf16(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_f16_fp8(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_bf16_fp8(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_f32_f32_large(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_f16_f16_large(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_bf16_bf16_large(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_f16_fp8_large(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_bf16_fp8_large(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_f16_int8(int d, int gh, bool balanced, bool append);
-KernelRef decode_kernels_bf16_int8(int d, int gh, bool balanced, bool append);
+KernelRef decode_kernels_f32_f32(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_f16_f16(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_bf16_bf16(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_f16_fp8(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_bf16_fp8(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_f32_f32_large(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_f16_f16_large(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_bf16_bf16_large(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_f16_fp8_large(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_bf16_fp8_large(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_f16_int8(int d, int gh, int kind, bool append);
+KernelRef decode_kernels_bf16_int8(int d, int gh, int kind, bool append);
 
 }  // namespace pa

@@ -307,3 +307,73 @@ def test_merge_many_pieces():
     wl = W.custom([16384, 9000, 3], 32, 8, 128, q_dtype="bf16", kv_dtype="fp8_e4m3fn", seed=23)
     for P in (256, -400):
         _check(wl, P, f"many pieces P={P}")
+
+
+ROW_WAVE_SHAPES = [(32, 8, 128, "bf16", "bf16"), (64, 8, 128, "bf16", "bf16"),
+                   (8, 8, 64, "f16", "f16"), (32, 8, 128, "bf16", "fp8_e4m3fn"),
+                   (16, 16, 128, "f16", "f16"), (32, 8, 64, "f16", "int8")]
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,qt,kt", ROW_WAVE_SHAPES)
+@pytest.mark.parametrize("P", [-1, -2, -7, -64])
+def test_row_wave_split_writes_every_output(Hq, Hkv, d, qt, kt, P):
+    """Head rows that fill eight-wave workgroups take the balanced split with
+    one wave per head row (every workgroup reads whole cache blocks). Every
+    output is written by pa_decode, the zeros of empty sequences included
+    (out starts as NaN), and matches the oracle."""
+    wl = W.custom([0, 33, 1, 700, 0, 16, 129, 2000, 0], Hq, Hkv, d, q_dtype=qt, kv_dtype=kt,
+                  seed=Hq + d - P)
+    print(f"[row waves] Hq={Hq} Hkv={Hkv} d={d} {qt}/{kt} P={P}", flush=True)
+    kc, vc, ref = oracle_step(wl)
+    dd = device_inputs(wl)
+    device_writes(wl, dd)
+    out = torch.full_like(dd["q"], float("nan"))
+    pa.decode(dd["q"], dd["k_cache"], dd["v_cache"], dd["block_tables"], dd["context_lens"],
+              scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale, partition_size=P, out=out)
+    torch.cuda.synchronize()
+    o = W.widen_to_f64(out)
+    assert (o[[0, 4, 8]] == 0).all()
+    assert_close(o, ref, wl.q_dtype, f"row waves P={P}")
+
+
+def test_row_wave_all_sequences_empty():
+    wl = W.custom([0, 0, 0], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", seed=2)
+    d = device_inputs(wl)
+    for P in (-1, -3):
+        out = torch.full_like(d["q"], float("nan"))
+        pa.decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                  partition_size=P, out=out)
+        assert (W.widen_to_f64(out) == 0).all()
+
+
+def test_split_reused_and_dirty_workspace():
+    """A workspace reused call after call, or full of arbitrary bytes, gives
+    bitwise the same output every time, within tolerance of the oracle; the
+    partials and the merge entry points called separately give the same
+    output too."""
+    wl = W.build("llama3_8b_b32")
+    kc, vc, ref = oracle_step(wl)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.head_dim,
+                                    wl.max_blocks_per_seq, wl.block_size, -1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for i in range(6):
+        if i == 3:  # arbitrary bytes, and counters that look like a running merge
+            ws.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda"))
+        outs.append(pa.decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                              d["context_lens"], scale=wl.scale, partition_size=-1,
+                              workspace=ws))
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs[1:])
+    assert_close(W.widen_to_f64(outs[0]), ref, wl.q_dtype, "reused workspace")
+    # the partials merged by the separate merge entry point give the same output
+    tmp, mx, sm = pa.decode_partials(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], -pa.decode_balanced_splits(
+                                         32, 8, 128, torch.bfloat16, torch.bfloat16),
+                                     scale=wl.scale)
+    red = pa.decode_reduce(tmp, mx, sm, d["context_lens"], -tmp.shape[1] + wl.num_seqs,
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(red, outs[0])
