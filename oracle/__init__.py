@@ -52,6 +52,7 @@ from .attention import (
     reduce_pieces,
 )
 from .cache_ops import reshape_and_cache, copy_blocks
+from .prefill import paged_prefill, prefill_flops
 from . import sizes
 
 __all__ = [
@@ -68,6 +69,8 @@ __all__ = [
     "balanced_pieces",
     "paged_decode_pieces",
     "reduce_pieces",
+    "paged_prefill",
+    "prefill_flops",
     "reshape_and_cache",
     "copy_blocks",
     "sizes",
