@@ -419,6 +419,57 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
                                   int kv_dtype, float k_scale, float v_scale, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/*
+ * pa_prefill -- paged prefill and chunked prefill: many new query tokens per
+ * sequence attend causally over the sequence's paged K/V.
+ *
+ * Prefill processes a request's input tokens and builds their K/V state
+ * before decode extends it one token at a time; a long input may be cut
+ * into chunks that are scheduled beside decode work ("vLLM inference
+ * principles", section on the two phases of one generation; "PagedAttention
+ * deep dive", section 1, on the compute/memory asymmetry of the phases).
+ * For sequence b let n = context_lens[b] and C = query_start[b + 1] -
+ * query_start[b]: the chunk is the sequence's last C tokens, their K/V
+ * already written to the cache (pa_reshape_and_cache), and query row
+ * query_start[b] + i (i < C) sits at position n - C + i. With g = h /
+ * (num_q_heads / num_kv_heads):
+ *
+ *   out[r, h] = softmax_j(scale * k_scale * < q[r, h], K[j] >) v_scale V[j]
+ *               over j = 0 .. n - C + i (causal),
+ *
+ * K[j] / V[j] being row (block_tables[b, j / block_size], j % block_size, g,
+ * :) of k_cache / v_cache ("KV-Cache evolution", sections 1 and 3A;
+ * "PagedAttention deep dive", section 2.1). C = n is a whole prompt; C = 1
+ * is one decode step.
+ *
+ *   out           [total_query_tokens, num_q_heads, head_dim], q_dtype; must
+ *                 not alias an input.
+ *   q             [total_query_tokens, num_q_heads, head_dim], f16 or bf16.
+ *   k_cache/v_cache [num_blocks, block_size, num_kv_heads, head_dim]: the
+ *                 query's type, or fp8_e4m3fn / int8 codes (k_scale,
+ *                 v_scale as in pa_decode); never written.
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; only the blocks
+ *                 holding positions < n are read.
+ *   context_lens  [num_seqs] int32.
+ *   query_start   [num_seqs + 1] int32, device: query_start[0] = 0,
+ *                 non-decreasing, query_start[num_seqs] = total_query_tokens,
+ *                 each chunk C <= n.
+ *   max_query_len at least the longest chunk (the launch grid covers this
+ *                 many query tokens per sequence).
+ *   scale         as in pa_decode (NaN: 1/sqrt(head_dim)).
+ * Supported: head_dim 64 or 128, the block sizes of pa_decode, any GQA group.
+ * The device-data preconditions (query_start, C <= n, block ids, n within
+ * the table) are unchecked. Errors as pa_decode; a zero chunk total is a
+ * no-op. Computed on MFMA with fp32 accumulation; the probabilities enter
+ * the P.V product rounded to the query's 16-bit type.
+ */
+pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens,
+                     const int32_t *query_start, int num_seqs, int total_query_tokens,
+                     int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                     int q_dtype, int kv_dtype, float k_scale, float v_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

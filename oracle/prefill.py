@@ -41,7 +41,7 @@ from .numerics import to_f64
 
 
 def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
-                  k_scale=1.0, v_scale=1.0):
+                  k_scale=1.0, v_scale=1.0, rows=None):
     """Causal attention of each chunk's query rows: float64 [T, Hq, d].
 
     q [T, Hq, d]; k_cache, v_cache [num_blocks, block_size, Hkv, d];
@@ -49,6 +49,8 @@ def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, 
     query_start [B + 1], non-decreasing, query_start[B] = T, and
     query_start[b + 1] - query_start[b] <= context_lens[b].
     ``scale`` is taken as the float32 value the caller passes, widened.
+    ``rows`` restricts the work to those query rows (the others stay NaN), so
+    that full-size workloads can be checked on samples.
     """
     q64 = to_f64(q)
     T, Hq, d = q64.shape
@@ -61,12 +63,13 @@ def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, 
     vs = float(np.float32(v_scale))
     qs = np.asarray(query_start, dtype=np.int64)
     assert qs[0] == 0 and qs[-1] == T and (np.diff(qs) >= 0).all()
-    out = np.zeros((T, Hq, d))
+    out = np.zeros((T, Hq, d)) if rows is None else np.full((T, Hq, d), np.nan)
+    wanted = None if rows is None else set(int(r) for r in rows)
     for b in range(len(context_lens)):
         n = int(context_lens[b])
         C = int(qs[b + 1] - qs[b])
         assert C <= n
-        if C == 0:
+        if C == 0 or (wanted is not None and not wanted & set(range(int(qs[b]), int(qs[b + 1])))):
             continue
         nblk = -(-n // bs)
         ids = np.asarray(block_tables[b][:nblk], dtype=np.int64)
@@ -75,6 +78,8 @@ def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, 
         for i in range(C):
             pos = n - C + i
             row = int(qs[b]) + i
+            if wanted is not None and row not in wanted:
+                continue
             for h in range(Hq):
                 g = h // group
                 s = (K[: pos + 1, g, :] @ q64[row, h]) * scale64

@@ -22,7 +22,7 @@ __all__ = [
     "ContractError", "set_debug_checks",
     "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3FN", "PA_INT8",
     "PaError", "lib", "library_path", "dtype_code",
-    "decode", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
+    "prefill", "decode", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
     "decode_shared_prefix", "decode_shared_prefix_workspace_size",
     "num_partitions", "decode_balanced_splits", "reshape_and_cache", "copy_blocks",
     "PARTITION_AUTO",
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 7 + [f32, f32, vp]
         L.pa_copy_blocks.restype = i32
         L.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
+        L.pa_prefill.restype = i32
+        L.pa_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i32, f32, f32, vp]
         L.pa_decode_shared_prefix_workspace_size.restype = sz
         L.pa_decode_shared_prefix_workspace_size.argtypes = [i32] * 7
         L.pa_decode_shared_prefix.restype = i32
@@ -238,6 +240,47 @@ def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
 
 def decode_noalloc_scratch_bytes() -> int:
     return lib().pa_decode_noalloc_scratch_bytes()
+
+
+def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+            max_query_len: Optional[int] = None, scale: Optional[float] = None,
+            k_scale: float = 1.0, v_scale: float = 1.0,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged (chunked) prefill (C: pa_prefill): rows query_start[b] ..
+    query_start[b + 1] - 1 of q [T, Hq, d] are the last tokens of sequence b's
+    context_lens[b] cached tokens and attend causally over them. Returns out
+    [T, Hq, d] in q's type. Without max_query_len the longest chunk is read
+    from a host copy of query_start (a synchronisation)."""
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise PaError("expected q [T, Hq, d] and caches [num_blocks, block_size, Hkv, d]")
+    T, Hq, d = q.shape
+    NB, bs, Hkv, d2 = k_cache.shape
+    B = context_lens.shape[0]
+    if d2 != d or block_tables.dim() != 2 or block_tables.shape[0] != B or \
+            query_start.shape != (B + 1,):
+        raise PaError("inconsistent shapes among q, caches, block_tables, context_lens, "
+                      "query_start")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    _i32(query_start, "query_start")
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
+        checks.check_query_start(query_start, context_lens, T)
+    if max_query_len is None:
+        qs = query_start.to("cpu")
+        max_query_len = int((qs[1:] - qs[:-1]).max()) if B else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PaError("out must match q in shape and type")
+    _check(lib().pa_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                            _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len), Hq,
+                            Hkv, d, bs, NB, block_tables.shape[1], _scale_arg(scale),
+                            dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
+                            _stream(dev)))
+    return out
 
 
 def decode_shared_prefix_workspace_size(num_seqs: int, num_groups: int, group_size: int,

@@ -27,6 +27,8 @@ The contracts (include/pa.h states each beside its entry point):
   (n - 1) is distinct, and the block holding it is private to that sequence
   (no other sequence's used block-table entries name it), since the launch
   writes that row while other workgroups read their own blocks;
+* prefill: query_start[0] = 0, non-decreasing, query_start[B] = the query
+  rows, and each chunk no longer than its sequence's context;
 * shared-prefix decode: members in [-1, num_seqs), each sequence in at most
   one slot; each group's whole-block prefix lies within every member's
   context and its table entries are the same physical blocks for every
@@ -39,7 +41,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["ContractError", "set_debug_checks", "debug_checks_enabled", "check_decode",
-           "check_slot_mapping", "check_block_mapping", "check_shared_prefix", "check_append"]
+           "check_slot_mapping", "check_block_mapping", "check_shared_prefix", "check_append",
+           "check_query_start"]
 
 
 class ContractError(ValueError):
@@ -174,3 +177,24 @@ def check_append(block_tables, context_lens, block_size: int) -> None:
         if others:
             raise ContractError(f"sequence {b} appends into block {last}, which sequence "
                                 f"{others[0]} also reads (copy the shared block first)")
+
+
+def check_query_start(query_start, context_lens, num_query_tokens: int) -> None:
+    """Prefill: the chunks tile the query rows in sequence order, and each
+    chunk (the last tokens of its sequence) fits in the sequence's context."""
+    qs = _host(query_start).astype(np.int64)
+    cl = _host(context_lens).astype(np.int64)
+    if qs.shape != (len(cl) + 1,):
+        raise ContractError(f"query_start has shape {qs.shape}, expected ({len(cl) + 1},)")
+    if qs[0] != 0 or qs[-1] != num_query_tokens:
+        raise ContractError(f"query_start must run from 0 to {num_query_tokens} "
+                            f"(got {int(qs[0])} .. {int(qs[-1])})")
+    c = np.diff(qs)
+    bad = np.nonzero(c < 0)[0]
+    if len(bad):
+        raise ContractError(f"query_start decreases at sequence {int(bad[0])}")
+    over = np.nonzero(c > cl)[0]
+    if len(over):
+        b = int(over[0])
+        raise ContractError(f"sequence {b}: chunk of {int(c[b])} tokens exceeds its context "
+                            f"of {int(cl[b])}")

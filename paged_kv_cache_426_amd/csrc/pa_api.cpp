@@ -534,3 +534,62 @@ pa_status pa_decode_shared_prefix(void *out, const void *q, const void *k_cache,
 }
 
 }  // extern "C"
+
+extern "C" {
+
+pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens,
+                     const int32_t *query_start, int num_seqs, int total_query_tokens,
+                     int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                     int q_dtype, int kv_dtype, float k_scale, float v_scale, void *stream) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL_POINTER;
+  if (num_seqs < 0 || total_query_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_ERR_BAD_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (!known_dtype(q_dtype) || !known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  // 16-bit queries; caches of the query's type or 8-bit codes
+  if (q_dtype != PA_F16 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype != q_dtype && !quantised(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || pa::sub_block_log2(block_size) < 0)
+    return PA_ERR_UNSUPPORTED;
+  if (isinf(scale)) return PA_ERR_BAD_SHAPE;
+  if (quantised(kv_dtype) && (!isfinite(k_scale) || !isfinite(v_scale))) return PA_ERR_BAD_SHAPE;
+  const long long row_bytes = (long long)num_kv_heads * head_dim * elem_bytes(kv_dtype);
+  if (row_bytes * 16 >= INT_MAX) return PA_ERR_UNSUPPORTED;
+  if ((long long)num_blocks * (block_size / 16) > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size > INT_MAX) return PA_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  const int tq = pa::prefill_tokens_per_tile(group);
+  const long long tiles = ((long long)max_query_len + tq - 1) / tq;
+  const long long grid_y = (long long)num_kv_heads * group / (128 / tq);
+  if (tiles > INT_MAX || grid_y > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  pa::PrefillLaunch a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.scale = resolve_scale(scale, head_dim);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  return status_of(pa::launch_prefill(a, stream));
+}
+
+}  // extern "C"
+

@@ -116,6 +116,22 @@ struct SharedPrefixLaunch {
 // Prep, prefix pass, suffix pass and merge, in stream order.
 int launch_shared_prefix(const SharedPrefixLaunch &a, void *stream);
 
+struct PrefillLaunch {
+  void *out;
+  const void *q, *k_cache, *v_cache;
+  const int32_t *block_tables, *context_lens, *query_start;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
+  int max_query_len;
+  float scale, k_scale, v_scale;
+  int q_dtype, kv_dtype;
+};
+
+// Causal attention of each sequence's chunk of query tokens over its paged
+// context (pa_prefill).
+int launch_prefill(const PrefillLaunch &a, void *stream);
+// Chunk tokens one prefill workgroup takes for a GQA group size.
+int prefill_tokens_per_tile(int group);
+
 // Shares a balanced split uses on the current device: enough workgroups to
 // fill every compute unit once at the decode kernel's occupancy.
 int balanced_num_splits(const DecodeLaunch &a);

@@ -225,3 +225,29 @@ def test_binding_refuses_cpu_tensors():
         pa.decode(q, kc, kc, bt, cl)
     with pytest.raises(pa.PaError, match="GPU tensors only"):
         pa.copy_blocks(kc, kc, torch.zeros(1, 2, dtype=torch.int64))
+
+
+def _prefill(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, B=2, T=10, maxq=8,
+                Hq=8, Hkv=2, d=128, bs=16, NB=16, MBS=4, scale=float("nan"), qt=pa.PA_BF16,
+                kt=pa.PA_BF16, ks=1.0, vs=1.0, stream=NULL)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"],
+                               a["B"], a["T"], a["maxq"], a["Hq"], a["Hkv"], a["d"], a["bs"],
+                               a["NB"], a["MBS"], a["scale"], a["qt"], a["kt"], a["ks"], a["vs"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=NULL), 1), (dict(out=NULL), 1),
+    (dict(Hq=7), 2), (dict(T=-1), 2), (dict(maxq=-1), 2), (dict(MBS=0), 2),
+    (dict(qt=pa.PA_F32, kt=pa.PA_F32), 3),           # 16-bit queries only
+    (dict(qt=pa.PA_BF16, kt=pa.PA_F16), 3),          # mixed 16-bit types
+    (dict(d=96), 3), (dict(bs=8), 3),
+    (dict(scale=float("inf")), 2),
+    (dict(kt=pa.PA_FP8_E4M3FN, ks=float("nan")), 2),
+    (dict(B=0), 0), (dict(T=0), 0), (dict(maxq=0), 0),   # nothing to do
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status

@@ -176,3 +176,14 @@ def test_planted_mistakes_are_caught(monkeypatch):
             except Exception:
                 continue
         assert not np.allclose(bad, want, atol=1e-9), f"slip not caught: {new}"
+
+
+def test_sampled_rows_match_full():
+    rng = np.random.default_rng(13)
+    q, K, V, kc, vc, table, cl, qs = _case(rng, [30, 12], [20, 5], 4, 2, 8, 8)
+    full = paged_prefill(q, kc, vc, table, cl, qs, 0.2)
+    part = paged_prefill(q, kc, vc, table, cl, qs, 0.2, rows=[3, 21])
+    assert np.array_equal(part[[3, 21]], full[[3, 21]])
+    keep = np.ones(len(q), bool)
+    keep[[3, 21]] = False
+    assert np.isnan(part[keep]).all()

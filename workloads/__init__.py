@@ -20,6 +20,10 @@ from .configs import (
     tiny_fp32_gqa2,
     permute_physical,
     unshare,
+    PrefillWorkload,
+    PREFILL_BUILDERS,
+    prefill_custom,
+    prefill_llama3_8b_b8,
 )
 
 __all__ = [
@@ -38,6 +42,10 @@ __all__ = [
     "shared_prefix_lens",
     "tiny_fp32_gqa2",
     "permute_physical",
+    "PrefillWorkload",
+    "PREFILL_BUILDERS",
+    "prefill_custom",
+    "prefill_llama3_8b_b8",
     "unshare",
     "to_device",
     "to_numpy",

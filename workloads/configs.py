@@ -497,3 +497,56 @@ def unshare(wl: Workload) -> Workload:
     return replace(wl, k_cache=k, v_cache=v, block_tables=tables, num_blocks=nb,
                    cow_pairs=np.zeros((0, 2), np.int64), hist_key=None, hist_value=None,
                    hist_slots=None, hist_seq=None, new_key=None, new_value=None, new_slots=None)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload:
+    """A cache state (``cache``: a decode Workload whose step writes fill every
+    sequence's context, chunk included) plus the chunks' query rows."""
+    name: str
+    cache: Workload
+    q: np.ndarray             # [T, Hq, d] (q dtype)
+    query_start: np.ndarray   # [B + 1] int32
+    chunk_lens: np.ndarray    # [B] int32
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.chunk_lens.max()) if len(self.chunk_lens) else 0
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+
+def prefill_custom(ctx_lens, chunk_lens, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16", bs=16,
+                   seed=0, extra_blocks=3, name="prefill_custom") -> PrefillWorkload:
+    """Sequences of ctx_lens cached tokens whose last chunk_lens tokens are
+    the chunk being prefilled. Values: fp32 N(0,1) rounded to the storage
+    types (8-bit caches through the slot write, as ``custom``)."""
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
+    chunk_lens = np.asarray(chunk_lens, dtype=np.int64)
+    assert (chunk_lens <= ctx_lens).all() and (chunk_lens >= 0).all()
+    wl = custom(ctx_lens, Hq, Hkv, d, q_dtype=q_dtype, kv_dtype=kv_dtype, bs=bs, seed=seed,
+                extra_blocks=extra_blocks, name=name)
+    rng = np.random.default_rng([426, 7, int(seed)])
+    qs = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int32)
+    q = normal(rng, (int(qs[-1]), Hq, d), q_dtype)
+    return PrefillWorkload(name=name, cache=wl, q=q, query_start=qs,
+                           chunk_lens=chunk_lens.astype(np.int32))
+
+
+def prefill_llama3_8b_b8(seed: int = 8, prefix: int = 2048, chunk: int = 2048,
+                         batch: int = 8) -> PrefillWorkload:
+    """Chunked prefill with Llama-3-8B attention shapes: 8 sequences, each a
+    2048-token chunk after a 2048-token cached prefix (contexts of 4096), 32
+    query / 8 KV heads, head_dim 128, bf16, 16-token blocks in a permuted
+    pool."""
+    return prefill_custom([prefix + chunk] * batch, [chunk] * batch, 32, 8, 128, "bf16", "bf16",
+                          seed=seed, name="prefill_llama3_8b_b8")
+
+
+PREFILL_BUILDERS = {"prefill_llama3_8b_b8": prefill_llama3_8b_b8}
