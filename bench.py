@@ -25,6 +25,8 @@ JSON line:
              8 TB/s
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
              workload, on this host's cores (a reported baseline only)
+  prefill    the chunked-prefill batch (8 x 2048-token chunks after 2048-token
+             prefixes, Llama-3-8B heads): pa_prefill against the MFMA roofline
   per_config every workload (tiny fp32, Llama-shaped, MHA, shared-prefix CoW,
              long-context fp8, and the same with an int8 cache) at its own
              launch configuration: decode time, KV tokens/s, GB/s and
@@ -472,6 +474,100 @@ def measure_config(wl, dev, args, stream, cpu_seconds):
     return e
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / f16 MFMA, published peak
+
+
+def prefill_flops(pw):
+    """Causal attention work of a prefill batch: per query head and attended
+    (query, key) pair, 2 d flops for q.k and 2 d for p.v; query i of a chunk
+    of C after n - C cached tokens attends n - C + i + 1 keys."""
+    wl = pw.cache
+    pairs = 0
+    for n, c in zip(wl.context_lens, pw.chunk_lens):
+        n, c = int(n), int(c)
+        pairs += c * (n - c) + c * (c + 1) // 2
+    return 4 * wl.head_dim * wl.num_q_heads * pairs
+
+
+def cpu_baseline_prefill(pw, budget_s):
+    """The prefill oracle as it stands on seeded sampled query rows of the
+    same batch, until the time budget is spent. Returns query tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    wl = pw.cache
+    kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+    if wl.hist_slots is not None and len(wl.hist_slots):
+        oracle.reshape_and_cache(wl.hist_key, wl.hist_value, kc, vc, wl.hist_slots,
+                                 wl.k_scale, wl.v_scale)
+    oracle.reshape_and_cache(wl.new_key, wl.new_value, kc, vc, wl.new_slots, wl.k_scale,
+                             wl.v_scale)
+    order = [int(r) for r in np.random.default_rng(0).permutation(pw.num_query_tokens)]
+    done, t_used = 0, 0.0
+    while t_used < budget_s and done < len(order):
+        rows = order[done:done + 16]
+        t0 = time.perf_counter()
+        oracle.paged_prefill(pw.q, kc, vc, wl.block_tables, wl.context_lens, pw.query_start,
+                             wl.scale, wl.k_scale, wl.v_scale, rows=rows)
+        t_used += time.perf_counter() - t0
+        done += len(rows)
+    return {"value": done / t_used, "unit": "query tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} seeded random query rows of {pw.name} (all {wl.num_q_heads} "
+                      f"heads each, float64 numpy), {t_used:.1f} s wall-clock"}
+
+
+def measure_prefill(name, dev, args, stream, cpu_seconds):
+    """The prefill batch: pa_prefill timed alone, against the MFMA roofline
+    (causal flops / time, dense bf16 peak)."""
+    import torch
+
+    import paged_kv_cache_426_amd as pa
+    import workloads as W
+
+    pw = W.PREFILL_BUILDERS[name]()
+    wl = pw.cache
+    layers = []
+    for _ in range(2):
+        prep = Prepared(wl, dev, 1)
+        kc, vc = prep.layers[0]
+        pa.reshape_and_cache(prep.new_k, prep.new_v, kc, vc, prep.new_s, wl.k_scale, wl.v_scale)
+        layers.append((kc, vc))
+    q = W.to_device(pw.q, dev)
+    qs = torch.as_tensor(pw.query_start, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    bt, cl = prep.bt, prep.cl
+    torch.cuda.synchronize()
+
+    def fn(i):
+        kc, vc = layers[i % 2]
+        pa.prefill(q, kc, vc, bt, cl, qs, max_query_len=pw.max_query_len, scale=wl.scale,
+                   k_scale=wl.k_scale, v_scale=wl.v_scale, out=out)
+    t = avg_launch_s(fn, 50, stream)
+    flops = prefill_flops(pw)
+    e = {
+        "workload": name,
+        "batch": wl.num_seqs,
+        "heads": f"{wl.num_q_heads}/{wl.num_kv_heads}/{wl.head_dim}",
+        "dtypes": f"{wl.q_dtype}/{wl.kv_dtype}",
+        "context_lens": sorted(set(int(x) for x in wl.context_lens)),
+        "chunk_lens": sorted(set(int(x) for x in pw.chunk_lens)),
+        "query_tokens": pw.num_query_tokens,
+        "prefill_us": t * 1e6,
+        "query_tokens_per_s": pw.num_query_tokens / t,
+        "roofline": {"bound": "mfma", "achieved": flops / t / 1e12,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "flops_per_launch": flops,
+                     "kernel": "prefill_kernel (one launch)"},
+    }
+    del layers, q, out, prep
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        e["cpu_baseline"] = cpu_baseline_prefill(pw, cpu_seconds)
+    return e
+
+
 PER_CONFIG = ("tiny_fp32_gqa2", "llama3_8b_b32", "mha_b32_ctx4096", "shared_prefix_cow_b64",
               "long_ctx_fp8_b8", "long_ctx_int8_b8")
 
@@ -694,6 +790,13 @@ def main(argv=None):
                 f"8 TB/s ({time.perf_counter() - t1:.1f} s)")
             per.append(e)
         result["per_config"] = per
+        t1 = time.perf_counter()
+        e = measure_prefill("prefill_llama3_8b_b8", dev, args, stream,
+                            0.0 if args.no_cpu_baseline else args.cpu_seconds_per_config)
+        log(f"prefill_llama3_8b_b8: {e['prefill_us']:.1f} us, "
+            f"{e['roofline']['achieved']:.0f} TFLOP/s = {e['roofline']['frac'] * 100:.1f} % of "
+            f"{MFMA_BF16_PEAK_TFLOPS:.0f} ({time.perf_counter() - t1:.1f} s)")
+        result["prefill"] = e
     print(json.dumps(result), flush=True)
     return 0
 

@@ -566,7 +566,7 @@ pa_status pa_prefill(void *out, const void *q, const void *k_cache, const void *
   const int tq = pa::prefill_tokens_per_tile(group);
   const long long tiles = ((long long)max_query_len + tq - 1) / tq;
   const long long grid_y = (long long)num_kv_heads * group / (128 / tq);
-  if (tiles > INT_MAX || grid_y > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (tiles * grid_y * num_seqs > (1ll << 30)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || total_query_tokens == 0 || max_query_len == 0) return PA_OK;
   pa::PrefillLaunch a{};
   a.out = out;

@@ -72,7 +72,9 @@ struct PrefillParams {
   int max_blocks_per_seq;
   int sub_log2;     // log2(block_size / 16)
   int group;        // query heads per KV head
-  int ntiles;       // query tiles per sequence in the grid (x)
+  int ntiles;       // query tiles per sequence
+  int rows_per_seq; // workgroups per sequence and query tile: KV heads x head subgroups
+  int num_seqs;
   float scale_log2; // scale * k_scale * log2(e)
   float v_scale;
 };
@@ -164,7 +166,8 @@ __device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 template <int QT, int KT, int D, int GH>
-__global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(const PrefillParams p) {
   constexpr int TQ = kPrefillRows / GH;       // chunk tokens per workgroup
   constexpr int KB = ElemBytes<KT>::value;    // cache element bytes
   constexpr int KRS = D * 2 + 16;             // LDS row stride of the K tile (16-bit)
@@ -183,10 +186,20 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(const Pr
   const int jq = lane >> 4;  // MFMA lane group
   const int tl = lane & 15;
 
-  // heaviest tiles (latest in the chunk: most keys) first
-  const int tile = p.ntiles - 1 - (int)blockIdx.x;
-  const int b = blockIdx.z;
-  const int hg = blockIdx.y;                 // (KV head, head subgroup)
+  // Work index: the launch is one-dimensional, and workgroup x runs on XCD
+  // x % 8 (the dispatcher deals workgroups to the XCDs in turn). Work item w
+  // goes to x = 8 (w % per) + w / per, so consecutive work items share an
+  // XCD; the query tiles of one (sequence, KV head) are consecutive, so they
+  // run together on one XCD and re-read their K/V from its L2. Within a
+  // (sequence, KV head) the heaviest tiles (latest in the chunk: most keys)
+  // come first.
+  const int total = p.ntiles * p.rows_per_seq * p.num_seqs;
+  const int per = (total + 7) / 8;
+  const int w = ((int)blockIdx.x % 8) * per + (int)blockIdx.x / 8;
+  if (w >= total) return;
+  const int tile = p.ntiles - 1 - w % p.ntiles;
+  const int hg = (w / p.ntiles) % p.rows_per_seq;  // (KV head, head subgroup)
+  const int b = w / p.ntiles / p.rows_per_seq;
   const int subgroups = p.group / GH;
   const int g = hg / subgroups;
   const int hbase = g * p.group + (hg % subgroups) * GH;
@@ -298,6 +311,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(const Pr
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[c][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const float sl2 = p.scale_log2;
+  const bool pos_scale = sl2 > 0.0f;
 
   int idn0 = sub_id(0), idn1 = sub_id(1);
   issue(0, idn0, idn1);
@@ -327,58 +341,101 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_kernel(const Pr
         for (int c = 0; c < 2; ++c) st[kt][c] = mfma32<QT>(a, qf[c][ss], st[kt][c]);
       }
     }
-    // online softmax of both column blocks; the probabilities of lane (tl,
-    // jq) become its P^T operand (keys 4 jq + e, e < 4, and 16 + 4 jq + e - 4)
-    u32x4 pb[2];
-    float alpha[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float sv[8];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const f32x4 x = st[kt][c];
-        const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * kt + 4 * jq + i;
-          sv[4 * kt + i] = key <= pos[c] ? xs[i] * sl2 : -INFINITY;
-        }
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[c], mx);
-      // a row that has seen no key yet keeps m = -inf: its probabilities and
-      // rescale are then zero
-      const float mref = mn == -INFINITY ? 0.0f : mn;
-      alpha[c] = __builtin_amdgcn_exp2f(m[c] - mref);
-      m[c] = mn;
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sv[i] = __builtin_amdgcn_exp2f(sv[i] - mref);
-        sum += sv[i];
-      }
-      l[c] = l[c] * alpha[c] + sum;
-      pb[c] = u32x4{pack16<QT>(sv[0], sv[1]), pack16<QT>(sv[2], sv[3]),
-                    pack16<QT>(sv[4], sv[5]), pack16<QT>(sv[6], sv[7])};
-    }
-    // O^T += V^T P^T per 16 output columns: V^T rows d = 16 dt + tl, keys in
-    // the same order as the probabilities
+    // Online softmax of both column blocks. Each row keeps a reference
+    // maximum m and the probabilities are exp2(s - m); m moves (and the
+    // row's sum and accumulators are rescaled) only when the row's maximum
+    // exceeds it by more than 8 (a factor 256), so probabilities stay below
+    // 256 and the rescale of the 64 accumulators is rare. The result is the
+    // same softmax (every term of a row carries the same factor 2^-m). Keys
+    // past a row's position are masked only in steps that reach past the
+    // tile's first row.
+    const bool diag = k0 + kPrefillKeys - 1 > pos0;
+    // V^T operands of the whole step (rows d = 16 dt + tl, keys 4 jq .. +3
+    // and 16 + 4 jq .. +3), read before the softmax so that the P.V MFMAs
+    // below never wait on LDS
+    u32x4 va[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const uint8_t *vr = &vsm[bf][(16 * dt + tl) * VRS];
       const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 8 * jq);
       const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 32 + 8 * jq);
-      const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+      va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    u32x4 pb[2];
+    float alpha[2] = {1.0f, 1.0f};
+    float sv[2][8];
+    bool ok[2][8];
+    float lm[2];  // this lane's largest scaled logit of the step, per block
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const f32x4 x = st[kt][c];
+        sv[c][4 * kt + 0] = x.x;
+        sv[c][4 * kt + 1] = x.y;
+        sv[c][4 * kt + 2] = x.z;
+        sv[c][4 * kt + 3] = x.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        ok[c][i] = !diag || k0 + 16 * (i / 4) + 4 * jq + i % 4 <= pos[c];
+      // the largest scaled logit: the largest raw logit times a positive
+      // scale, the smallest times a negative or zero one; masked keys never win
+      float e;
+      if (pos_scale) {
+        e = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e = fmaxf(e, ok[c][i] ? sv[c][i] : -INFINITY);
+      } else {
+        e = INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e = fminf(e, ok[c][i] ? sv[c][i] : INFINITY);
+      }
+      lm[c] = __builtin_isinf(e) ? -INFINITY : e * sl2;
+    }
+    // A row's reference maximum m moves only when the row's maximum exceeds
+    // it by more than 8: unless some lane's own maximum does, no row moves
+    // and the row reductions are skipped (the usual case once every row has
+    // seen its first keys).
+    const bool any_up = __builtin_amdgcn_ballot_w64(lm[0] > m[0] + 8.0f || lm[1] > m[1] + 8.0f) != 0;
+    if (any_up) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        o[c][dt] *= alpha[c];
-        o[c][dt] = mfma32<QT>(va, pb[c], o[c][dt]);
+        float mx = lm[c];
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool up = mx > m[c] + 8.0f;
+        const float mn = up ? mx : m[c];
+        alpha[c] = up ? __builtin_amdgcn_exp2f(m[c] - mn) : 1.0f;
+        m[c] = mn;
+        l[c] *= alpha[c];
       }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[c][dt] *= alpha[c];
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // a row that has seen no key yet keeps m = -inf and gets no weight
+      const float mref = m[c] == -INFINITY ? 0.0f : m[c];
+      float sum = 0.0f;
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sv[c][i], sl2, -mref));
+        pr[i] = ok[c][i] ? e : 0.0f;
+        sum += pr[i];
+      }
+      l[c] += sum;
+      pb[c] = u32x4{pack16<QT>(pr[0], pr[1]), pack16<QT>(pr[2], pr[3]),
+                    pack16<QT>(pr[4], pr[5]), pack16<QT>(pr[6], pr[7])};
+    }
+    // O^T += V^T P^T per 16 output columns
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) o[c][dt] = mfma32<QT>(va[dt], pb[c], o[c][dt]);
   }
 
   // ---- normalise and write: lane holds row (c, tl), elements 16 dt + 4 jq + 0..3
@@ -464,7 +521,11 @@ int launch_prefill(const PrefillLaunch &a, void *stream) {
   const void *fn = prefill_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh);
   if (!fn) return (int)hipErrorInvalidValue;
   if (p.ntiles == 0) return 0;
-  const dim3 grid(p.ntiles, a.num_kv_heads * (p.group / gh), a.num_seqs);
+  p.rows_per_seq = a.num_kv_heads * (p.group / gh);
+  p.num_seqs = a.num_seqs;
+  const long long total = (long long)p.ntiles * p.rows_per_seq * a.num_seqs;
+  if (total > (1ll << 30)) return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)(8 * ((total + 7) / 8)));
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(fn, grid, dim3(kPrefillWaves * kWave), args, 0,
                                  static_cast<hipStream_t>(stream));
