@@ -236,13 +236,39 @@ void prefill_kernel(const PrefillParams p) {
   const uint32_t rowstride = (uint32_t)p.num_kv_heads * D * KB;  // bytes per token row
   const uint32_t blk_bytes = rowstride * 16;
   const uint32_t span = blk_bytes - (uint32_t)g * D * KB;         // head g's rows to the block end
-  const int32_t *table = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  // The block-table row, read with vector loads: a scalar load would share
+  // its wait counter with the LDS reads of the steps and stall them for a
+  // memory round trip.
+  const __amdgpu_buffer_rsrc_t trow = rsrc(
+      reinterpret_cast<const uint8_t *>(p.block_tables + (size_t)b * p.max_blocks_per_seq),
+      (uint32_t)p.max_blocks_per_seq * 4u);
   const int smask = (1 << p.sub_log2) - 1;
-  // physical 16-token sub-block of logical sub-block j (0 past the last one
-  // the tile reads; its loads are then of nothing)
-  auto sub_id = [&](int j) {
-    if (j * 16 > plast) return 0;
-    return (table[j >> p.sub_log2] << p.sub_log2) + (j & smask);
+  // Physical 16-token sub-block ids, 64 per register: lane i of chunk c
+  // holds sub-block 64 c + i (0 past the last one the tile reads; its loads
+  // are then of nothing). The next chunk is loaded a chunk (32 steps) ahead,
+  // and a step takes its two ids with readlane.
+  auto load_chunk = [&](int c) {
+    const int j = 64 * c + lane;
+    const bool in = j * 16 <= plast;
+    const int e = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        trow, (uint32_t)(in ? (j >> p.sub_log2) : 0) * 4u, 0, 0);
+    return in ? (e << p.sub_log2) + (j & smask) : 0;
+  };
+  int ch_idx = 0;
+  int ch_cur = load_chunk(0);
+  int ch_nxt = load_chunk(1);
+  auto ids_of = [&](int s, int &id0, int &id1) {  // sub-blocks 2 s and 2 s + 1
+    const int j0 = 2 * s;
+    const bool next = (j0 >> 6) != ch_idx;
+    if (next) {
+      ch_cur = ch_nxt;
+      ++ch_idx;
+    }
+    id0 = __builtin_amdgcn_readlane(ch_cur, j0 & 63);
+    id1 = __builtin_amdgcn_readlane(ch_cur, (j0 + 1) & 63);
+    // the following chunk's load goes out after the ids are taken, so that
+    // nothing waits for it
+    if (next) ch_nxt = load_chunk(ch_idx + 1);
   };
   auto sub_rsrc = [&](const uint8_t *cache, int j, int id) {
     const uint32_t bytes = j * 16 <= plast ? span : 0u;
@@ -257,7 +283,9 @@ void prefill_kernel(const PrefillParams p) {
   // 4 or 8 consecutive keys of K, 8 or 16 of V, aligned), so each load's
   // buffer resource is wave-uniform (a per-lane resource would make the
   // compiler loop over the distinct values).
-  auto issue = [&](int s, int id0, int id1) {
+  auto issue = [&](int s) {
+    int id0, id1;
+    ids_of(s, id0, id1);
 #pragma unroll
     for (int i = 0; i < KPIECES; ++i) {
       const int pc = tid + i * kPrefillWaves * kWave;
@@ -313,19 +341,12 @@ void prefill_kernel(const PrefillParams p) {
   const float sl2 = p.scale_log2;
   const bool pos_scale = sl2 > 0.0f;
 
-  int idn0 = sub_id(0), idn1 = sub_id(1);
-  issue(0, idn0, idn1);
-  idn0 = sub_id(2);
-  idn1 = sub_id(3);
+  issue(0);
   for (int s = 0; s < nsteps; ++s) {
     const int bf = s & 1;
     stash(s, bf);
     __syncthreads();
-    if (s + 1 < nsteps) {
-      issue(s + 1, idn0, idn1);
-      idn0 = sub_id(2 * s + 4);
-      idn1 = sub_id(2 * s + 5);
-    }
+    if (s + 1 < nsteps) issue(s + 1);
     const int k0 = kPrefillKeys * s;
     // S^T = K Q^T for both 16-key tiles and both column blocks
     f32x4 st[2][2];
