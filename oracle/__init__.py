@@ -15,7 +15,8 @@ Array conventions (the stored element type is carried by the numpy dtype):
 * ``float16``  -- IEEE binary16 values;
 * ``uint16``   -- bfloat16 bit patterns;
 * ``uint8``    -- OCP E4M3FN (fp8) codes;
-* ``int8``     -- symmetric int8 codes (value = code x the tensor's scale).
+* ``int8``     -- symmetric int8 codes (value = code x the tensor's scale, or
+  x the scale of the code's block and head, see ``scaled``).
 
 Sources, cited by page title and section (all four pages are about the KV
 cache and PagedAttention):
@@ -50,9 +51,16 @@ from .attention import (
     balanced_pieces,
     paged_decode_pieces,
     reduce_pieces,
+    widen_blocks,
 )
 from .cache_ops import reshape_and_cache, copy_blocks
 from .prefill import paged_prefill, prefill_flops
+from .scaled import (
+    expand_scales,
+    reshape_and_cache_scaled,
+    reshape_and_cache_scaled_bulk,
+    copy_blocks_scaled,
+)
 from . import sizes
 
 __all__ = [
@@ -69,6 +77,11 @@ __all__ = [
     "balanced_pieces",
     "paged_decode_pieces",
     "reduce_pieces",
+    "widen_blocks",
+    "expand_scales",
+    "reshape_and_cache_scaled",
+    "reshape_and_cache_scaled_bulk",
+    "copy_blocks_scaled",
     "paged_prefill",
     "prefill_flops",
     "reshape_and_cache",

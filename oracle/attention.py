@@ -48,8 +48,21 @@ def gather_logical_kv(cache_f64: np.ndarray, block_table_row: np.ndarray, n: int
     return rows.reshape(nblk * bs, *cache_f64.shape[2:])[:n]
 
 
+def widen_blocks(cache, ids, block_scales=None) -> np.ndarray:
+    """Physical blocks ``ids`` of a cache as float64 [len(ids), bs, Hkv, d]:
+    the stored values widened exactly and, when a scale table
+    ``block_scales`` [num_blocks, Hkv] is given (an 8-bit cache with a scale
+    per block and head, see ``oracle.scaled``), each row multiplied by the
+    scale of its own physical block and KV head."""
+    x = to_f64(cache[ids])
+    if block_scales is not None:
+        x = x * np.asarray(block_scales, dtype=np.float64)[ids][:, None, :, None]
+    return x
+
+
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
-                 k_scale=1.0, v_scale=1.0, seqs=None, heads=None):
+                 k_scale=1.0, v_scale=1.0, seqs=None, heads=None,
+                 k_block_scales=None, v_block_scales=None):
     """Decode attention for every (sequence, query head): float64 [B, Hq, d].
 
     ``scale`` is the softmax scale (normally 1/sqrt(d)), taken as the float32
@@ -60,6 +73,8 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
 
     ``seqs`` / ``heads`` restrict the work to a subset (the rest of the output
     stays NaN) so that full-size workloads can be checked on samples.
+    ``k_block_scales`` / ``v_block_scales`` ([num_blocks, Hkv], see
+    ``widen_blocks``) give each block and head its own dequantisation scale.
     """
     q64 = to_f64(q)
     B, Hq, d = q64.shape
@@ -80,8 +95,8 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
         nblk = -(-n // k_cache.shape[1])
         ids = np.asarray(block_tables[b][:nblk], dtype=np.int64)
         # widen only the blocks this sequence uses
-        K = gather_logical_kv(to_f64(k_cache[ids]), np.arange(nblk), n) * ks
-        V = gather_logical_kv(to_f64(v_cache[ids]), np.arange(nblk), n) * vs
+        K = gather_logical_kv(widen_blocks(k_cache, ids, k_block_scales), np.arange(nblk), n) * ks
+        V = gather_logical_kv(widen_blocks(v_cache, ids, v_block_scales), np.arange(nblk), n) * vs
         for h in heads:
             g = h // group
             s = (K[:, g, :] @ q64[b, h]) * scale64
@@ -191,13 +206,15 @@ def balanced_pieces(context_lens, block_size, num_splits):
 
 
 def paged_decode_pieces(q, k_cache, v_cache, block_tables, context_lens, scale, pieces,
-                        k_scale=1.0, v_scale=1.0, unit=None):
+                        k_scale=1.0, v_scale=1.0, unit=None, k_block_scales=None,
+                        v_block_scales=None):
     """(m, l, o~) of each piece (s, b, first_block, end_block) for every query
     head: the softmax statistics of the piece's own tokens
     [first_block * u, min(end_block * u, n)), as in paged_decode_partials,
     where u = unit, the number of tokens the piece bounds count in (the
     cache's block size unless given; the library's balanced split counts
-    16-token sub-blocks whatever the block size).
+    16-token sub-blocks whatever the block size). Block scales as in
+    ``paged_decode``.
     Shapes: m, l [len(pieces), Hq]; o~ [len(pieces), Hq, d]."""
     q64 = to_f64(q)
     B, Hq, d = q64.shape
@@ -213,8 +230,8 @@ def paged_decode_pieces(q, k_cache, v_cache, block_tables, context_lens, scale, 
         n = int(context_lens[b])
         nblk = -(-n // bs)
         ids = np.asarray(block_tables[b][:nblk], dtype=np.int64)
-        K = gather_logical_kv(to_f64(k_cache[ids]), np.arange(nblk), n) * ks
-        V = gather_logical_kv(to_f64(v_cache[ids]), np.arange(nblk), n) * vs
+        K = gather_logical_kv(widen_blocks(k_cache, ids, k_block_scales), np.arange(nblk), n) * ks
+        V = gather_logical_kv(widen_blocks(v_cache, ids, v_block_scales), np.arange(nblk), n) * vs
         u = bs if unit is None else int(unit)
         lo, hi = fb * u, min(eb * u, n)
         for h in range(Hq):
