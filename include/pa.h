@@ -50,9 +50,8 @@
  * sharing article" sections 2 and 4), any block size for the slot write and
  * the block copy; any num_q_heads that is a multiple of num_kv_heads; (q, kv)
  * element types (f32, f32), (f16, f16), (bf16, bf16), (f16, fp8_e4m3fn),
- * (bf16, fp8_e4m3fn), (f16, int8), (bf16, int8) (int8 caches: decode with
- * block_size 16). Decode reads a block of 16 * 2^k tokens as 2^k consecutive
- * 16-token sub-blocks.
+ * (bf16, fp8_e4m3fn), (f16, int8), (bf16, int8). Decode reads a block of
+ * 16 * 2^k tokens as 2^k consecutive 16-token sub-blocks.
  */
 #ifndef PA_H
 #define PA_H
@@ -79,7 +78,9 @@ typedef enum pa_status {
  * int8 is a symmetric int8 code c in [-127, 127] standing for c * scale (the
  * pages name INT8 and FP8 KV quantisation: "PagedAttention deep dive",
  * section 4; "KV-Cache evolution", section 3C). Both 8-bit types are cache
- * types only, with one fp32 scale per tensor (k_scale, v_scale). */
+ * types only, with one fp32 scale per tensor (k_scale, v_scale), or with a
+ * table of scales per KV head, per block or per (block, KV head) (the
+ * *_scaled entry points below). */
 typedef enum pa_dtype {
   PA_F32 = 0,
   PA_F16 = 1,
@@ -361,6 +362,98 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
                          int num_pairs, int num_kv_heads, int head_dim, int block_size,
                          int num_blocks, int cache_dtype, void *stream);
+
+/*
+ * 8-bit caches with scale tables.
+ *
+ * The pages name INT8 and FP8 storage of the KV cache, combined with paging,
+ * to shrink each cache unit ("PagedAttention deep dive", section 4 item 1;
+ * "KV-Cache evolution", section 3C; "KV-cache sharing article", section 6),
+ * but not the granularity of the scales. Besides one scale per tensor, the
+ * library takes a table of float32 scales, one per KV head, per physical
+ * block, or per (physical block, KV head): a code c of KV head g in physical
+ * block e stands for value(c) * S[e, g], where S is the table read through
+ * its layout:
+ *
+ *   PA_SCALE_PER_HEAD        k_scales[num_kv_heads]:            S[e, g] = k_scales[g]
+ *   PA_SCALE_PER_BLOCK       k_scales[num_blocks]:              S[e, g] = k_scales[e]
+ *   PA_SCALE_PER_BLOCK_HEAD  k_scales[num_blocks, num_kv_heads]: S[e, g] = k_scales[e, g]
+ *
+ * and likewise v_scales for V. A block's scales are the scales of its
+ * contents: the slot write quantises with them, decode dequantises with
+ * them, and a copy-on-write copy carries them to the new block. How the
+ * scales are chosen (e.g. a block's largest magnitude over the codec's
+ * largest code, fixed before the block's first write) is the caller's
+ * policy; the library only applies them. The tables are device memory;
+ * their values are not checked (a zero, negative or non-finite scale gives
+ * the corresponding non-finite or sign-flipped values).
+ */
+typedef enum pa_scale_layout {
+  PA_SCALE_PER_HEAD = 1,
+  PA_SCALE_PER_BLOCK = 2,
+  PA_SCALE_PER_BLOCK_HEAD = 3
+} pa_scale_layout;
+
+/*
+ * pa_reshape_and_cache_scaled -- pa_reshape_and_cache into an 8-bit cache
+ * with scale tables: for each token t with s = slot_mapping[t] >= 0 and each
+ * KV head g, with e = s / block_size,
+ *   k_cache[e, s % block_size, g, :] = enc(key[t, g, :], S_k[e, g])
+ *   v_cache[e, s % block_size, g, :] = enc(value[t, g, :], S_v[e, g])
+ * with enc as in pa_reshape_and_cache (correctly rounded float32 division,
+ * round to nearest even, saturation).
+ *
+ *   cache_dtype   PA_FP8_E4M3FN or PA_INT8; src_dtype f32, f16 or bf16, with
+ *                 head_dim * sizeof(src element) a multiple of 16 bytes.
+ *   k_scales, v_scales  device float32 tables of scale_layout (read only).
+ * Errors: PA_ERR_NULL_POINTER for missing tables; PA_ERR_BAD_SHAPE for an
+ * unknown layout; PA_ERR_UNSUPPORTED for other cache or source types; others
+ * as pa_reshape_and_cache.
+ */
+pa_status pa_reshape_and_cache_scaled(const void *key, const void *value, void *k_cache,
+                                      void *v_cache, const int64_t *slot_mapping,
+                                      int num_tokens, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int src_dtype,
+                                      int cache_dtype, const float *k_scales,
+                                      const float *v_scales, int scale_layout, void *stream);
+
+/*
+ * pa_copy_blocks_scaled -- pa_copy_blocks for an 8-bit cache with scale
+ * tables: each pair copies the block's codes and, for PA_SCALE_PER_BLOCK
+ * and PA_SCALE_PER_BLOCK_HEAD, its scale entries (k_scales[dst] =
+ * k_scales[src], one entry or num_kv_heads entries; likewise v_scales), all
+ * from the state before the call. A PA_SCALE_PER_HEAD table has no
+ * per-block entries and is not touched. Errors as pa_copy_blocks, plus
+ * PA_ERR_NULL_POINTER for missing tables and PA_ERR_BAD_SHAPE for an unknown
+ * layout.
+ */
+pa_status pa_copy_blocks_scaled(void *k_cache, void *v_cache, float *k_scales, float *v_scales,
+                                const int64_t *block_mapping, int num_pairs, int num_kv_heads,
+                                int head_dim, int block_size, int num_blocks, int cache_dtype,
+                                int scale_layout, void *stream);
+
+/*
+ * pa_decode_scaled -- pa_decode over an 8-bit cache with scale tables:
+ *
+ *   s_j      = scale * S_k[e_j, g] * < q[b, h, :], K[j] >
+ *   out[b,h] = sum_j exp(s_j - max s) S_v[e_j, g] V[j] / sum_j exp(s_j - max s)
+ *
+ * where e_j = block_tables[b, j / block_size] is the physical block holding
+ * token j and K[j], V[j] are its codes' values. Arguments, splitting,
+ * workspace and errors as pa_decode, with kv_dtype PA_FP8_E4M3FN or PA_INT8
+ * (PA_ERR_UNSUPPORTED otherwise) and the tables in place of k_scale /
+ * v_scale (PA_ERR_NULL_POINTER when missing, PA_ERR_BAD_SHAPE for an unknown
+ * layout). The decode kernels multiply each 16-token unit's logits by its
+ * block's K scale and its probabilities by its V scale before P.V (the
+ * softmax sums use the probabilities alone).
+ */
+pa_status pa_decode_scaled(void *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                           int q_dtype, int kv_dtype, const float *k_scales,
+                           const float *v_scales, int scale_layout, int partition_size,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_decode_shared_prefix -- decode for groups of sequences that share a

@@ -25,6 +25,8 @@ __all__ = [
     "prefill", "decode", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_append", "decode_partials", "decode_reduce", "decode_workspace_size",
     "decode_shared_prefix", "decode_shared_prefix_workspace_size",
     "num_partitions", "decode_balanced_splits", "reshape_and_cache", "copy_blocks",
+    "decode_scaled", "reshape_and_cache_scaled", "copy_blocks_scaled",
+    "PA_SCALE_PER_HEAD", "PA_SCALE_PER_BLOCK", "PA_SCALE_PER_BLOCK_HEAD",
     "PARTITION_AUTO",
 ]
 
@@ -32,6 +34,9 @@ __all__ = [
 PARTITION_AUTO = -1
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3FN, PA_INT8 = 0, 1, 2, 3, 4
+
+# layouts of the scale tables of an 8-bit cache (pa.h pa_scale_layout)
+PA_SCALE_PER_HEAD, PA_SCALE_PER_BLOCK, PA_SCALE_PER_BLOCK_HEAD = 1, 2, 3
 
 _DTYPES = {
     torch.float32: PA_F32,
@@ -95,6 +100,13 @@ def lib() -> ctypes.CDLL:
         L.pa_reshape_and_cache.argtypes = [vp] * 5 + [i32] * 7 + [f32, f32, vp]
         L.pa_copy_blocks.restype = i32
         L.pa_copy_blocks.argtypes = [vp] * 3 + [i32] * 6 + [vp]
+        L.pa_decode_scaled.restype = i32
+        L.pa_decode_scaled.argtypes = ([vp] * 6 + [i32] * 7 + [f32, i32, i32, vp, vp, i32, i32,
+                                                              vp, sz, vp])
+        L.pa_reshape_and_cache_scaled.restype = i32
+        L.pa_reshape_and_cache_scaled.argtypes = [vp] * 5 + [i32] * 7 + [vp, vp, i32, vp]
+        L.pa_copy_blocks_scaled.restype = i32
+        L.pa_copy_blocks_scaled.argtypes = [vp] * 5 + [i32] * 7 + [vp]
         L.pa_prefill.restype = i32
         L.pa_prefill.argtypes = [vp] * 7 + [i32] * 9 + [f32, i32, i32, f32, f32, vp]
         L.pa_decode_shared_prefix_workspace_size.restype = sz
@@ -457,3 +469,89 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
                                 block_mapping.shape[0], Hkv, d, bs, NB, dtype_code(k_cache),
                                 _stream(dev)))
+
+
+def _scale_tables(k_scales: torch.Tensor, v_scales: torch.Tensor, layout: int, num_blocks: int,
+                  num_kv_heads: int) -> None:
+    """Checks that the two scale tables are float32 and shaped for ``layout``."""
+    want = {PA_SCALE_PER_HEAD: (num_kv_heads,), PA_SCALE_PER_BLOCK: (num_blocks,),
+            PA_SCALE_PER_BLOCK_HEAD: (num_blocks, num_kv_heads)}.get(int(layout))
+    if want is None:
+        raise PaError(f"unknown scale layout {layout}")
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t.dtype != torch.float32 or tuple(t.shape) != want:
+            raise PaError(f"{name} must be float32 {list(want)} for layout {layout}")
+
+
+def decode_scaled(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  k_scales: torch.Tensor, v_scales: torch.Tensor, scale_layout: int,
+                  scale: Optional[float] = None, partition_size: int = 0,
+                  out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode over an 8-bit cache with scale tables per KV head, per block or
+    per (block, KV head) (C: pa_decode_scaled). Returns out [B, Hq, d]."""
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, k_scales, v_scales, out,
+               workspace)
+    B, Hq, d, NB, bs, Hkv, MBS = _decode_shapes(q, k_cache, v_cache, block_tables, context_lens)
+    _scale_tables(k_scales, v_scales, scale_layout, NB, Hkv)
+    if checks.debug_checks_enabled():
+        checks.check_decode(block_tables, context_lens, NB, bs)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise PaError("out must match q in shape and type")
+    need = decode_workspace_size(B, Hq, d, MBS, bs, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_scaled(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, d, bs, NB,
+                                  MBS, _scale_arg(scale), dtype_code(q), dtype_code(k_cache),
+                                  _ptr(k_scales), _ptr(v_scales), int(scale_layout),
+                                  int(partition_size), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def reshape_and_cache_scaled(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                             k_scales: torch.Tensor, v_scales: torch.Tensor,
+                             scale_layout: int) -> None:
+    """Slot write into an 8-bit cache, each row quantised with its block's
+    (and head's) scale (C: pa_reshape_and_cache_scaled)."""
+    dev = _dev(key, value, k_cache, v_cache, slot_mapping, k_scales, v_scales)
+    _i64(slot_mapping, "slot_mapping")
+    if key.dim() != 3 or value.shape != key.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or key.shape[1:] != k_cache.shape[2:] or \
+            slot_mapping.shape != (key.shape[0],) or value.dtype != key.dtype or \
+            v_cache.dtype != k_cache.dtype:
+        raise PaError("expected key/value [N, Hkv, d], caches [num_blocks, bs, Hkv, d], slots [N]")
+    N, Hkv, d = key.shape
+    NB, bs = k_cache.shape[:2]
+    _scale_tables(k_scales, v_scales, scale_layout, NB, Hkv)
+    if checks.debug_checks_enabled():
+        checks.check_slot_mapping(slot_mapping, NB, bs)
+    _check(lib().pa_reshape_and_cache_scaled(_ptr(key), _ptr(value), _ptr(k_cache),
+                                             _ptr(v_cache), _ptr(slot_mapping), N, Hkv, d, bs, NB,
+                                             dtype_code(key), dtype_code(k_cache),
+                                             _ptr(k_scales), _ptr(v_scales), int(scale_layout),
+                                             _stream(dev)))
+
+
+def copy_blocks_scaled(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
+                       v_scales: torch.Tensor, scale_layout: int,
+                       block_mapping: torch.Tensor) -> None:
+    """Copy-on-write copies of blocks and their scales (C: pa_copy_blocks_scaled)."""
+    dev = _dev(k_cache, v_cache, k_scales, v_scales, block_mapping)
+    _i64(block_mapping, "block_mapping")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2 or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise PaError("expected caches [num_blocks, bs, Hkv, d] and block_mapping [P, 2]")
+    NB, bs, Hkv, d = k_cache.shape
+    _scale_tables(k_scales, v_scales, scale_layout, NB, Hkv)
+    if checks.debug_checks_enabled():
+        checks.check_block_mapping(block_mapping, NB)
+    _check(lib().pa_copy_blocks_scaled(_ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+                                       _ptr(v_scales), _ptr(block_mapping),
+                                       block_mapping.shape[0], Hkv, d, bs, NB,
+                                       dtype_code(k_cache), int(scale_layout), _stream(dev)))

@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libpa.so")
 PAIRS = ["f32_f32", "f16_f16", "bf16_bf16", "f16_fp8", "bf16_fp8"]
 SOURCES = (["pa_api.cpp", "pa_decode.hip", "pa_cache.hip", "pa_prefix.hip", "pa_prefill.hip"] +
            [f"pa_decode_{p}.hip" for p in PAIRS] + [f"pa_decode_{p}_large.hip" for p in PAIRS] +
-           ["pa_decode_f16_int8.hip", "pa_decode_bf16_int8.hip"])
+           ["pa_decode_f16_int8.hip", "pa_decode_bf16_int8.hip",
+            "pa_decode_f16_int8_large.hip", "pa_decode_bf16_int8_large.hip"])
 
 ARCH = "gfx950"
 

@@ -55,8 +55,6 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
   if (isinf(scale)) return PA_ERR_BAD_SHAPE;  // NaN: the default scale
   if (quantised(kv_dtype) && (!isfinite(k_scale) || !isfinite(v_scale)))
     return PA_ERR_BAD_SHAPE;
-  // int8 decode kernels are built for 16-token blocks only
-  if (kv_dtype == PA_INT8 && block_size != 16) return PA_ERR_UNSUPPORTED;
   // launch-grid and in-kernel 32-bit offset limits
   const long long row_bytes = (long long)num_kv_heads * head_dim * elem_bytes(kv_dtype);
   if (row_bytes * block_size >= INT_MAX) return PA_ERR_UNSUPPORTED;
@@ -213,14 +211,21 @@ pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_log
 
 namespace {
 
-// pa_decode, and pa_decode_append when new_k / new_v are given.
+// Scale tables of pa_decode_scaled (k == nullptr: per-tensor scales).
+struct Tables {
+  const float *k, *v;
+  int block_stride, head_stride;
+};
+
+// pa_decode, pa_decode_append when new_k / new_v are given, and
+// pa_decode_scaled with scale tables.
 pa_status decode_impl(void *out, const void *q, const void *new_k, const void *new_v,
                       const void *k_cache, const void *v_cache, const int32_t *block_tables,
                       const int32_t *context_lens, int num_seqs, int num_q_heads,
                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
                       int max_blocks_per_seq, float scale, int q_dtype, int kv_dtype,
                       float k_scale, float v_scale, int partition_size, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+                      size_t workspace_bytes, void *stream, const Tables &tables = {}) {
   if (!out) return PA_ERR_NULL_POINTER;
   pa_status st = check_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
@@ -249,6 +254,10 @@ pa_status decode_impl(void *out, const void *q, const void *new_k, const void *n
   a.kv_dtype = kv_dtype;
   a.partition_size = partition_size;
   a.direct = 1;
+  a.k_scales = tables.k;
+  a.v_scales = tables.v;
+  a.scale_block_stride = tables.block_stride;
+  a.scale_head_stride = tables.head_stride;
   size_t need = 0;
   size_t pieces = 0;  // partial-array entries per (sequence, head) or per head
   if (partition_size > 0) {
@@ -343,6 +352,25 @@ pa_status pa_decode_noalloc(void *out, const void *q, const void *k_cache, const
 
 size_t pa_decode_noalloc_scratch_bytes(void) { return pa::kNoallocScratchBytes; }
 
+pa_status pa_decode_scaled(void *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                           int q_dtype, int kv_dtype, const float *k_scales,
+                           const float *v_scales, int scale_layout, int partition_size,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (!k_scales || !v_scales) return PA_ERR_NULL_POINTER;
+  Tables t{k_scales, v_scales, 0, 0};
+  if (num_kv_heads > 0 &&
+      !pa::scale_strides(scale_layout, num_kv_heads, &t.block_stride, &t.head_stride))
+    return PA_ERR_BAD_SHAPE;
+  if (known_dtype(kv_dtype) && !quantised(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, scale, q_dtype, kv_dtype, 1.0f, 1.0f, partition_size,
+                     workspace, workspace_bytes, stream, t);
+}
+
 pa_status pa_decode_append(void *out, const void *q, const void *key, const void *value,
                            void *k_cache, void *v_cache, const int32_t *block_tables,
                            const int32_t *context_lens, int num_seqs, int num_q_heads,
@@ -383,7 +411,38 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *k_cache
   if (num_tokens == 0) return PA_OK;
   return status_of(pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
                                                 num_tokens, num_kv_heads, head_dim, src_dtype,
-                                                cache_dtype, k_scale, v_scale, stream));
+                                                cache_dtype, k_scale, v_scale,
+                                                pa::ScaleTables{}, stream));
+}
+
+pa_status pa_reshape_and_cache_scaled(const void *key, const void *value, void *k_cache,
+                                      void *v_cache, const int64_t *slot_mapping,
+                                      int num_tokens, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int src_dtype,
+                                      int cache_dtype, const float *k_scales,
+                                      const float *v_scales, int scale_layout, void *stream) {
+  if (!k_scales || !v_scales) return PA_ERR_NULL_POINTER;
+  pa::ScaleTables t{const_cast<float *>(k_scales), const_cast<float *>(v_scales), 0, 0,
+                    block_size};
+  if (num_kv_heads > 0 &&
+      !pa::scale_strides(scale_layout, num_kv_heads, &t.block_stride, &t.head_stride))
+    return PA_ERR_BAD_SHAPE;
+  if (known_dtype(cache_dtype) && !quantised(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  if (known_dtype(src_dtype) && quantised(src_dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0 && k_cache && v_cache) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_BAD_SHAPE;
+  if (!known_dtype(src_dtype) || !known_dtype(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  // a 16-byte piece of the source never spans two heads (one scale per piece)
+  if ((long long)head_dim * elem_bytes(src_dtype) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  const long long row_src_bytes = (long long)num_kv_heads * head_dim * elem_bytes(src_dtype);
+  if (row_src_bytes > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  return status_of(pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+                                                num_tokens, num_kv_heads, head_dim, src_dtype,
+                                                cache_dtype, 1.0f, 1.0f, t, stream));
 }
 
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
@@ -399,7 +458,30 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapp
   if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   return status_of(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, block_bytes,
-                                          stream));
+                                          nullptr, nullptr, 0, stream));
+}
+
+pa_status pa_copy_blocks_scaled(void *k_cache, void *v_cache, float *k_scales, float *v_scales,
+                                const int64_t *block_mapping, int num_pairs, int num_kv_heads,
+                                int head_dim, int block_size, int num_blocks, int cache_dtype,
+                                int scale_layout, void *stream) {
+  if (!k_scales || !v_scales) return PA_ERR_NULL_POINTER;
+  int sb = 0, sh = 0;
+  if (num_kv_heads > 0 && !pa::scale_strides(scale_layout, num_kv_heads, &sb, &sh))
+    return PA_ERR_BAD_SHAPE;
+  if (known_dtype(cache_dtype) && !quantised(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0 && k_cache && v_cache) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL_POINTER;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_BAD_SHAPE;
+  if (!known_dtype(cache_dtype)) return PA_ERR_UNSUPPORTED;
+  const size_t block_bytes =
+      (size_t)block_size * num_kv_heads * head_dim * (size_t)elem_bytes(cache_dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  // entries per block: the table's block stride (0 for a per-head table)
+  return status_of(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, block_bytes,
+                                          k_scales, v_scales, sb, stream));
 }
 
 

@@ -121,27 +121,20 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
   store_elem<OT>(p.out, bh * D + d, O / W);
 }
 
-KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, int kind,
-                            bool append, bool large) {
-  if (q_dtype == PA_F32 && kv_dtype == PA_F32)
-    return large ? decode_kernels_f32_f32_large(d, gh, kind, append)
-                 : decode_kernels_f32_f32(d, gh, kind, append);
-  if (q_dtype == PA_F16 && kv_dtype == PA_F16)
-    return large ? decode_kernels_f16_f16_large(d, gh, kind, append)
-                 : decode_kernels_f16_f16(d, gh, kind, append);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16)
-    return large ? decode_kernels_bf16_bf16_large(d, gh, kind, append)
-                 : decode_kernels_bf16_bf16(d, gh, kind, append);
-  if (q_dtype == PA_F16 && kv_dtype == PA_FP8_E4M3FN)
-    return large ? decode_kernels_f16_fp8_large(d, gh, kind, append)
-                 : decode_kernels_f16_fp8(d, gh, kind, append);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3FN)
-    return large ? decode_kernels_bf16_fp8_large(d, gh, kind, append)
-                 : decode_kernels_bf16_fp8(d, gh, kind, append);
-  if (q_dtype == PA_F16 && kv_dtype == PA_INT8 && !large)
-    return decode_kernels_f16_int8(d, gh, kind, append);
-  if (q_dtype == PA_BF16 && kv_dtype == PA_INT8 && !large)
-    return decode_kernels_bf16_int8(d, gh, kind, append);
+KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, int kind, bool append,
+                            bool large, bool scaled) {
+#define PA_PAIR(Q, KV, NAME)                                                                   \
+  if (q_dtype == Q && kv_dtype == KV)                                                          \
+    return large ? decode_kernels_##NAME##_large(d, gh, kind, append, scaled)                  \
+                 : decode_kernels_##NAME(d, gh, kind, append, scaled);
+  PA_PAIR(PA_F32, PA_F32, f32_f32)
+  PA_PAIR(PA_F16, PA_F16, f16_f16)
+  PA_PAIR(PA_BF16, PA_BF16, bf16_bf16)
+  PA_PAIR(PA_F16, PA_FP8_E4M3FN, f16_fp8)
+  PA_PAIR(PA_BF16, PA_FP8_E4M3FN, bf16_fp8)
+  PA_PAIR(PA_F16, PA_INT8, f16_int8)
+  PA_PAIR(PA_BF16, PA_INT8, bf16_int8)
+#undef PA_PAIR
   return {nullptr, 0};
 }
 
@@ -186,12 +179,14 @@ BalancedChoice balanced_kernel(const DecodeLaunch &a, bool append, bool large) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int gh = heads_per_workgroup(group);
   const long long rows = (long long)a.num_kv_heads * (group / gh);
+  const bool scaled = a.k_scales != nullptr;
   if (rows % 8 == 0) {
     const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRowWaves,
-                                          append, large);
+                                          append, large, scaled);
     if (k.fn) return {k, true, (int)(rows / 8)};
   }
-  return {decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindShares, append, large),
+  return {decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindShares, append, large,
+                            scaled),
           false, (int)rows};
 }
 
@@ -236,9 +231,16 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.direct = a.direct;
   p.group = a.num_q_heads / a.num_kv_heads;
   const bool q8 = a.kv_dtype == PA_FP8_E4M3FN || a.kv_dtype == PA_INT8;
-  const float ks = q8 ? a.k_scale : 1.0f;
+  // scale tables: each block's scales are applied per block in the kernel
+  const bool scaled = a.k_scales != nullptr;
+  const bool tensor_scales = q8 && !scaled;
+  const float ks = tensor_scales ? a.k_scale : 1.0f;
   p.scale_log2 = a.scale * ks * kLog2e;
-  p.v_scale = q8 ? a.v_scale : 1.0f;
+  p.v_scale = tensor_scales ? a.v_scale : 1.0f;
+  p.k_scales = a.k_scales;
+  p.v_scales = a.v_scales;
+  p.scale_sb = a.scale_block_stride;
+  p.scale_sh = a.scale_head_stride;
   p.new_k = static_cast<const uint8_t *>(a.new_k);
   p.new_v = static_cast<const uint8_t *>(a.new_v);
   p.k_cache_w = const_cast<uint8_t *>(p.k_cache);
@@ -257,7 +259,8 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
     grid = c.row_waves ? dim3(p.num_splits, c.rowgroups, 1)
                        : dim3((p.num_splits + 1) / 2, head_groups, 1);
   } else {
-    k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRanges, append, large);
+    k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRanges, append, large,
+                          scaled);
     grid = a.mode == kSplitFixed ? dim3(a.max_partitions, head_groups, a.num_seqs)
                                  : dim3(1, head_groups, a.num_seqs);
   }

@@ -4,8 +4,8 @@
 
 namespace pa {
 
-KernelRef decode_kernels_bf16_bf16_large(int d, int gh, int kind, bool append) {
-  return by_d<PA_BF16, PA_BF16, true>(d, gh, kind, append);
+KernelRef decode_kernels_bf16_bf16_large(int d, int gh, int kind, bool append, bool scaled) {
+  return by_d<PA_BF16, PA_BF16, true>(d, gh, kind, append, scaled);
 }
 
 }  // namespace pa

@@ -4,8 +4,8 @@
 
 namespace pa {
 
-KernelRef decode_kernels_f16_fp8(int d, int gh, int kind, bool append) {
-  return by_d<PA_F16, PA_FP8_E4M3FN, false>(d, gh, kind, append);
+KernelRef decode_kernels_f16_fp8(int d, int gh, int kind, bool append, bool scaled) {
+  return by_d<PA_F16, PA_FP8_E4M3FN, false>(d, gh, kind, append, scaled);
 }
 
 }  // namespace pa

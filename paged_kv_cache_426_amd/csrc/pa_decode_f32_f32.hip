@@ -4,8 +4,8 @@
 
 namespace pa {
 
-KernelRef decode_kernels_f32_f32(int d, int gh, int kind, bool append) {
-  return by_d<PA_F32, PA_F32, false>(d, gh, kind, append);
+KernelRef decode_kernels_f32_f32(int d, int gh, int kind, bool append, bool scaled) {
+  return by_d<PA_F32, PA_F32, false>(d, gh, kind, append, scaled);
 }
 
 }  // namespace pa

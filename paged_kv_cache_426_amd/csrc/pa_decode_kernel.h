@@ -111,6 +111,12 @@ struct DecodeParams {
   uint8_t *k_cache_w;
   uint8_t *v_cache_w;
   float k_scale, v_scale_w;
+  // scale tables of an 8-bit cache (kernels built with SC): the scale of
+  // (physical block e, KV head g) is k_scales[e * scale_sb + g * scale_sh];
+  // scale_log2 and v_scale then carry no cache scale
+  const float *k_scales;
+  const float *v_scales;
+  int scale_sb, scale_sh;
 };
 
 // ---------------------------------------------------------------------------
@@ -486,6 +492,8 @@ struct Item {
 struct Ids {
   int entry;  // block-table entry
   int sub;    // 16-token sub-block within that block
+  int ok;     // the lane holds a unit's block (scale tables only)
+  float ks, vs;  // that block's K and V scales for the segment's KV head (scale tables only)
 };
 
 struct Seg {
@@ -510,7 +518,8 @@ struct Seg {
 // first unit of the next segment is already being loaded (its block ids and
 // query fragments were fetched one segment ahead), so a switch between
 // ranges costs only the epilogue of the finished range.
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB, bool RW>
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB, bool RW,
+          bool SC>
 __device__ __forceinline__ void run_ranges(const DecodeParams &p,
                                            Shared<QT, KT, D, GH, NBI, NW> &sh, const Item (&items)[2],
                                            int n_items, int b_first, int n_first, int blo_first,
@@ -610,8 +619,19 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     const bool ok = sg.valid && kk < sg.nk && j < sg.bhi;
     const int32_t *row = p.block_tables + (size_t)(sg.valid ? sg.b : 0) * p.max_blocks_per_seq;
     const int e = ok ? j : 0;
-    if constexpr (SUB) return Ids{row[e >> p.sub_log2], e & ((1 << p.sub_log2) - 1)};
-    else return Ids{row[e], 0};
+    if constexpr (SUB) return Ids{row[e >> p.sub_log2], e & ((1 << p.sub_log2) - 1), ok, 0.f, 0.f};
+    else return Ids{row[e], 0, ok, 0.f, 0.f};
+  };
+  // scale tables: each lane's block scales for KV head g, loaded where the
+  // segment's ids are first used (their load is long done by then); lanes
+  // holding no unit read entry 0
+  auto load_scales = [&](Ids &ids, int g) {
+    if constexpr (SC) {
+      const size_t i =
+          ids.ok ? (size_t)ids.entry * p.scale_sb + (size_t)g * p.scale_sh : (size_t)0;
+      ids.ks = p.k_scales[i];
+      ids.vs = p.v_scales[i];
+    }
   };
   // the appended token of sg's sequence, when sg's range holds it (loads
   // are issued in any case, of nothing otherwise)
@@ -725,9 +745,26 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   };
 
   auto compute_unit = [&](int jb, int tok_lim, const QOp (&qa)[G::ksteps], const St &st,
-                          const AE &app, int g, bool writer) {
+                          const AE &app, int g, bool writer, const Ids &ids, int u) {
     // logits, log2 domain; masked tokens -inf
     float sv[NBI][4];
+    // per block: the logit factor (the softmax scale in the log2 domain,
+    // times the block's K scale with scale tables) and the V scale that
+    // multiplies the block's probabilities in P.V (not in the sums l)
+    float lf[NBI], vsc[NBI];
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi) {
+      if constexpr (SC) {
+        const int li = u * NBI + bi;
+        lf[bi] = sl2 * __builtin_bit_cast(
+                           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.ks), li));
+        vsc[bi] = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.vs), li));
+      } else {
+        lf[bi] = sl2;
+        vsc[bi] = 1.0f;
+      }
+    }
     // K tile: registers (row-contiguous) -> LDS -> MFMA operand layout, in
     // which lane (tl, jq) holds bytes k_byte(i, jq) of token row tl
 #pragma unroll
@@ -773,10 +810,10 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 #pragma unroll
       for (int s = 0; s < G::ksteps; ++s) d = mfma<QT>(qa[s], k_operand<QT, KT, D>(kop, s), d);
       const bool ok = (jb + bi) * kBs + tl < tok_lim;
-      sv[bi][0] = ok ? d.x * sl2 : -INFINITY;
-      sv[bi][1] = ok ? d.y * sl2 : -INFINITY;
-      sv[bi][2] = ok ? d.z * sl2 : -INFINITY;
-      sv[bi][3] = ok ? d.w * sl2 : -INFINITY;
+      sv[bi][0] = ok ? d.x * lf[bi] : -INFINITY;
+      sv[bi][1] = ok ? d.y * lf[bi] : -INFINITY;
+      sv[bi][2] = ok ? d.z * lf[bi] : -INFINITY;
+      sv[bi][3] = ok ? d.w * lf[bi] : -INFINITY;
     }
     // online softmax per MFMA row v (head (4*jq + v) % GH)
     float al[4];
@@ -804,7 +841,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (v < GH) sh.p[wave][bi * kBs + tl][4 * jq + v] = sv[bi][v];
+          if (v < GH) sh.p[wave][bi * kBs + tl][4 * jq + v] = SC ? sv[bi][v] * vsc[bi] : sv[bi][v];
       if (tl == 0) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -1095,6 +1132,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   Seg nxt = next_seg(cur);
   if constexpr (APP) app_nxt = load_app(nxt);
   St st[NS];
+  load_scales(ids_cur, cur.g);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(ids_cur, s, s < cur.kn, cur.g, st[s]);
   Ids ids_nxt = fetch_ids(nxt);
@@ -1121,7 +1159,8 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         const int u = k + s + NS - 1;
         issue(ids_cur, u, u < kn, g_cur, st[(s + NS - 1) % NS]);
         if (k + s < kn) {
-          compute_unit(jb0 + (k + s) * ND * NBI, tok_lim, q_cur, st[s], app, g_cur, writer);
+          compute_unit(jb0 + (k + s) * ND * NBI, tok_lim, q_cur, st[s], app, g_cur, writer,
+                       ids_cur, k + s);
           pace();
         }
       }
@@ -1129,6 +1168,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     // the last step, peeled: it issues this segment's last unit and the
     // next segment's first NS - 1 units (so that the ids of the next
     // segment are read only here, where their load is long done)
+    load_scales(ids_nxt, g_nxt);
     {
       const int k = kpad - NS;
 #pragma unroll
@@ -1136,7 +1176,8 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         if (s == 0) issue(ids_cur, kpad - 1, kpad - 1 < kn, g_cur, st[NS - 1]);
         else issue(ids_nxt, s - 1, nxt.valid && s - 1 < nxt.kn, g_nxt, st[s - 1]);
         if (k + s < kn) {
-          compute_unit(jb0 + (k + s) * ND * NBI, tok_lim, q_cur, st[s], app, g_cur, writer);
+          compute_unit(jb0 + (k + s) * ND * NBI, tok_lim, q_cur, st[s], app, g_cur, writer,
+                       ids_cur, k + s);
           pace();
         }
       }
@@ -1163,7 +1204,8 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 
 }
 
-template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB, bool RW>
+template <int QT, int KT, int D, int GH, int NBI, int NS, int NW, bool APP, bool SUB, bool RW,
+          bool SC>
 __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p) {
   __shared__ Shared<QT, KT, D, GH, NBI, NW> sh;
   const int tid = threadIdx.x;
@@ -1287,7 +1329,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
     first_piece = items[0].share + first_b;
     first_whole = first_lo == 0 && first_hi == en - st;
   }
-  run_ranges<QT, KT, D, GH, NBI, NS, NW, APP, SUB, RW>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
+  run_ranges<QT, KT, D, GH, NBI, NS, NW, APP, SUB, RW, SC>(p, sh, items, n_items, first_b, first_n, first_lo, first_hi,
                                      first_piece, first_whole);
 }
 
@@ -1320,69 +1362,77 @@ constexpr int balanced_waves() {
 // ranges (single pass or fixed partitions), balanced shares dealt to all
 // waves of a workgroup, or balanced shares with one wave per head row (built
 // where eight waves fit the registers; {nullptr, 0} otherwise).
-template <int QT, int KT, int D, int GH, bool APP, bool SUB>
+template <int QT, int KT, int D, int GH, bool APP, bool SUB, bool SC>
 KernelRef kernel_of(int kind) {
   constexpr int NBI = units_of<QT, KT, GH>();
   constexpr int NWB = balanced_waves<QT, KT, D, GH, APP>();
   if (kind == kKindRowWaves) {
     if constexpr (NWB == 8)
       return {reinterpret_cast<const void *>(
-                  &decode_kernel<QT, KT, D, GH, NBI, kStages, 8, APP, SUB, true>),
+                  &decode_kernel<QT, KT, D, GH, NBI, kStages, 8, APP, SUB, true, SC>),
               8 * kWave};
     return {nullptr, 0};
   }
   if (kind == kKindShares)
     return {reinterpret_cast<const void *>(
-                &decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP, SUB, false>),
+                &decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP, SUB, false, SC>),
             NWB * kWave};
   return {reinterpret_cast<const void *>(
-              &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP, SUB, false>),
+              &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP, SUB, false, SC>),
           kFixedWaves * kWave};
 }
 
+// scaled: kernels for 8-bit caches with scale tables (built without append)
 template <int QT, int KT, int D, int GH, bool SUB>
-KernelRef with_append(int kind, bool append) {
-  return append ? kernel_of<QT, KT, D, GH, true, SUB>(kind)
-                : kernel_of<QT, KT, D, GH, false, SUB>(kind);
+KernelRef with_append(int kind, bool append, bool scaled) {
+  if (scaled) {
+    if constexpr (ElemBytes<KT>::value == 1)
+      if (!append) return kernel_of<QT, KT, D, GH, false, SUB, true>(kind);
+    return {nullptr, 0};
+  }
+  return append ? kernel_of<QT, KT, D, GH, true, SUB, false>(kind)
+                : kernel_of<QT, KT, D, GH, false, SUB, false>(kind);
 }
 
 template <int QT, int KT, int D, bool SUB>
-KernelRef by_gh(int gh, int kind, bool append) {
+KernelRef by_gh(int gh, int kind, bool append, bool scaled) {
   switch (gh) {
-    case 1: return with_append<QT, KT, D, 1, SUB>(kind, append);
-    case 2: return with_append<QT, KT, D, 2, SUB>(kind, append);
-    case 4: return with_append<QT, KT, D, 4, SUB>(kind, append);
-    case 8: return with_append<QT, KT, D, 8, SUB>(kind, append);
-    case 16: return with_append<QT, KT, D, 16, SUB>(kind, append);
+    case 1: return with_append<QT, KT, D, 1, SUB>(kind, append, scaled);
+    case 2: return with_append<QT, KT, D, 2, SUB>(kind, append, scaled);
+    case 4: return with_append<QT, KT, D, 4, SUB>(kind, append, scaled);
+    case 8: return with_append<QT, KT, D, 8, SUB>(kind, append, scaled);
+    case 16: return with_append<QT, KT, D, 16, SUB>(kind, append, scaled);
   }
   return {nullptr, 0};
 }
 
 template <int QT, int KT, bool SUB>
-KernelRef by_d(int d, int gh, int kind, bool append) {
+KernelRef by_d(int d, int gh, int kind, bool append, bool scaled) {
   switch (d) {
-    case 64: return by_gh<QT, KT, 64, SUB>(gh, kind, append);
-    case 128: return by_gh<QT, KT, 128, SUB>(gh, kind, append);
+    case 64: return by_gh<QT, KT, 64, SUB>(gh, kind, append, scaled);
+    case 128: return by_gh<QT, KT, 128, SUB>(gh, kind, append, scaled);
   }
   return {nullptr, 0};
 }
 }  // namespace
 
 // The kernels of one element-type pair: the decode kernel for head size d,
-// gh query heads per workgroup, a KernelKind, with append or not;
-// {nullptr, 0} when not built. Each pair has one translation unit for
-// 16-token blocks and one (_large) for larger blocks.
-KernelRef decode_kernels_f32_f32(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_f16_f16(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_bf16_bf16(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_f16_fp8(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_bf16_fp8(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_f32_f32_large(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_f16_f16_large(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_bf16_bf16_large(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_f16_fp8_large(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_bf16_fp8_large(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_f16_int8(int d, int gh, int kind, bool append);
-KernelRef decode_kernels_bf16_int8(int d, int gh, int kind, bool append);
+// gh query heads per workgroup, a KernelKind, with append or not, with scale
+// tables or not; {nullptr, 0} when not built. Each pair has one translation
+// unit for 16-token blocks and one (_large) for larger blocks.
+KernelRef decode_kernels_f32_f32(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f16_f16(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_bf16_bf16(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f16_fp8(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_bf16_fp8(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f32_f32_large(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f16_f16_large(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_bf16_bf16_large(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f16_fp8_large(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_bf16_fp8_large(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f16_int8(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_f16_int8_large(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_bf16_int8(int d, int gh, int kind, bool append, bool scaled);
+KernelRef decode_kernels_bf16_int8_large(int d, int gh, int kind, bool append, bool scaled);
 
 }  // namespace pa

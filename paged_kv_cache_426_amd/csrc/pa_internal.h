@@ -53,7 +53,24 @@ struct DecodeLaunch {
   // these rows; null for a plain decode
   const void *new_k;
   const void *new_v;
+  // 8-bit caches with scale tables (pa_decode_scaled): the scale of
+  // (physical block e, KV head g) is k_scales[e * scale_block_stride +
+  // g * scale_head_stride] (likewise v_scales); null for per-tensor scales
+  const float *k_scales;
+  const float *v_scales;
+  int scale_block_stride, scale_head_stride;
 };
+
+// Strides of a scale table of the given layout (a pa.h PA_SCALE_* value)
+// over (physical block, KV head); false for an unknown layout.
+inline bool scale_strides(int layout, int num_kv_heads, int *block_stride, int *head_stride) {
+  switch (layout) {
+    case 1: *block_stride = 0; *head_stride = 1; return true;             // [Hkv]
+    case 2: *block_stride = 1; *head_stride = 0; return true;             // [num_blocks]
+    case 3: *block_stride = num_kv_heads; *head_stride = 1; return true;  // [num_blocks, Hkv]
+  }
+  return false;
+}
 
 struct ReduceLaunch {
   void *out;
@@ -79,12 +96,22 @@ struct KernelRef {
 // Each returns 0 on success or the runtime's error code.
 int launch_decode(const DecodeLaunch &a, void *stream);
 int launch_reduce(const ReduceLaunch &a, void *stream);
+// Scale tables of the slot write and the block copy: null for per-tensor
+// scales (slot write) or none to move (copy); strides as in DecodeLaunch.
+struct ScaleTables {
+  float *k, *v;
+  int block_stride, head_stride;
+  int block_size;  // tokens per physical block (slot write: slot / block_size)
+};
+
 int launch_reshape_and_cache(const void *key, const void *value, void *k_cache, void *v_cache,
                              const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
                              int head_dim, int src_dtype, int cache_dtype, float k_scale,
-                             float v_scale, void *stream);
+                             float v_scale, const ScaleTables &tables, void *stream);
+// entries: scale entries per block to copy (0: none; 1 or Hkv)
 int launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping,
-                       int num_pairs, size_t block_bytes, void *stream);
+                       int num_pairs, size_t block_bytes, float *k_scales, float *v_scales,
+                       int entries, void *stream);
 
 // Device scratch of a shared-prefix decode, carved from the caller's workspace.
 struct SharedPrefixWorkspace {

@@ -83,7 +83,6 @@ def _decode(**kw):
     (dict(qt=pa.PA_BF16, kt=pa.PA_F16), 3),        # mixed 16-bit types
     (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),  # fp8 cache needs a 16-bit query
     (dict(qt=pa.PA_F32, kt=pa.PA_INT8), 3),        # int8 cache needs a 16-bit query
-    (dict(qt=pa.PA_BF16, kt=pa.PA_INT8, bs=32), 3),  # int8 decode: 16-token blocks only
     (dict(qt=pa.PA_BF16, kt=pa.PA_INT8, vs=float("nan")), 2),
     (dict(qt=7), 3),
     (dict(P=24), 2),                               # not a multiple of block_size
@@ -106,6 +105,60 @@ def test_decode_validation(kw, status):
 def test_zero_sequences_is_a_no_op():
     assert _decode(B=0) == 0
     assert _decode(B=0, scale=float("nan")) == 0   # the default scale passes validation
+    # int8 caches at every decode block size pass validation
+    for bs in (16, 32, 64, 128, 256):
+        assert _decode(B=0, qt=pa.PA_BF16, kt=pa.PA_INT8, bs=bs) == 0
+
+
+def _scaled(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=2, Hq=4, Hkv=2, d=128,
+                bs=16, NB=16, MBS=4, scale=float("nan"), qt=pa.PA_BF16, kt=pa.PA_INT8,
+                kss=FAKE, vss=FAKE, layout=pa.PA_SCALE_PER_BLOCK_HEAD, P=0, ws=NULL, wsb=0,
+                stream=NULL)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_decode_scaled(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["B"],
+                                     a["Hq"], a["Hkv"], a["d"], a["bs"], a["NB"], a["MBS"],
+                                     a["scale"], a["qt"], a["kt"], a["kss"], a["vss"],
+                                     a["layout"], a["P"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kss=NULL), 1), (dict(vss=NULL), 1), (dict(out=NULL), 1),
+    (dict(layout=0), 2), (dict(layout=4), 2),      # unknown scale layout
+    (dict(kt=pa.PA_BF16), 3),                      # scale tables: 8-bit caches only
+    (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),
+    (dict(Hq=3), 2), (dict(d=96), 3), (dict(bs=8), 3),
+    (dict(P=16), 1),                               # split without workspace
+    (dict(P=-4, ws=FAKE, wsb=10), 4),
+    (dict(B=0), 0),                                # no sequences: no-op
+    (dict(B=0, kt=pa.PA_FP8_E4M3FN, layout=pa.PA_SCALE_PER_HEAD, bs=256), 0),
+])
+def test_decode_scaled_validation(kw, status):
+    assert _scaled(**kw) == status
+
+
+def test_reshape_and_copy_scaled_validation():
+    L = pa.lib()
+    rc = L.pa_reshape_and_cache_scaled
+    i8, bf = pa.PA_INT8, pa.PA_BF16
+    lay = pa.PA_SCALE_PER_BLOCK_HEAD
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, bf, i8, NULL, FAKE, lay, NULL) == 1
+    assert rc(NULL, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, bf, i8, FAKE, FAKE, lay, NULL) == 1
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, bf, i8, FAKE, FAKE, 9, NULL) == 2
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, bf, bf, FAKE, FAKE, lay, NULL) == 3
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 16, 4, i8, i8, FAKE, FAKE, lay, NULL) == 3
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 2, 64, 16, 4, bf, i8, FAKE, FAKE, lay, NULL) == 2
+    # a head row must be whole 16-byte pieces of the source (one scale per piece)
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 4, 16, 4, bf, i8, FAKE, FAKE, lay, NULL) == 3
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 64, 16, 4, bf, i8, FAKE, FAKE, lay, NULL) == 0
+    cb = L.pa_copy_blocks_scaled
+    assert cb(FAKE, FAKE, NULL, FAKE, FAKE, 1, 2, 64, 16, 4, i8, lay, NULL) == 1
+    assert cb(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 16, 4, i8, 0, NULL) == 2
+    assert cb(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 16, 4, bf, lay, NULL) == 3
+    assert cb(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 2, 64, 16, 4, i8, lay, NULL) == 2
+    assert cb(FAKE, FAKE, FAKE, FAKE, NULL, 1, 2, 64, 16, 4, i8, lay, NULL) == 1
+    assert cb(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 64, 16, 4, i8, lay, NULL) == 0
 
 
 def _append(**kw):

@@ -20,7 +20,8 @@ from _helpers import assert_close, device_inputs, device_step, device_writes, or
 pytestmark = pytest.mark.gpu
 
 CTX = [1, 15, 16, 17, 63, 64, 65, 129, 255, 256, 257, 511, 513, 1025]
-PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3fn")]
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3fn"),
+         ("f16", "int8"), ("bf16", "int8")]
 
 
 def _check(wl, P, what):
@@ -66,10 +67,11 @@ def _as_16_token_blocks(wl):
                    block_tables=bt16, new_slots=slots)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
 @pytest.mark.parametrize("bs", [32, 64, 256])
 @pytest.mark.parametrize("P", [0, 256, -1, -7])
-def test_large_blocks_equal_their_16_token_view_bitwise(bs, P):
-    wl = W.custom(CTX, 8, 2, 128, q_dtype="bf16", kv_dtype="bf16", bs=bs, seed=3 * bs)
+def test_large_blocks_equal_their_16_token_view_bitwise(bs, P, kv):
+    wl = W.custom(CTX, 8, 2, 128, q_dtype="bf16", kv_dtype=kv, bs=bs, seed=3 * bs)
     wl16 = _as_16_token_blocks(wl)
     print(f"[block size] bs={bs} vs its 16-token view, P={P}", flush=True)
     _, out = device_step(wl, P)

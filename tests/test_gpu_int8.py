@@ -117,12 +117,32 @@ def test_int8_decode_append_equals_write_then_decode(P):
     assert torch.equal(sep, fused)
 
 
-def test_int8_large_blocks_are_refused():
-    wl = W.custom([40], 8, 2, 128, q_dtype="bf16", kv_dtype="int8", bs=32, seed=1)
-    d = device_inputs(wl)
-    with pytest.raises(pa.PaError):
-        pa.decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                  k_scale=wl.k_scale, v_scale=wl.v_scale)
+@pytest.mark.parametrize("bs", [32, 256])
+def test_int8_large_blocks_with_append(bs):
+    """int8 caches of 32- to 256-token blocks through decode with the new
+    token appended: caches and output bitwise equal to the slot write
+    followed by decode, and within tolerance of the oracle."""
+    wl = W.custom([1, 40, 300, 513, 0], 8, 2, 128, q_dtype="bf16", kv_dtype="int8", bs=bs,
+                  seed=bs)
+    kc, vc, ref = oracle_step(wl)
+    for P in (0, bs, -1):
+        print(f"[int8] bs={bs} append P={P}", flush=True)
+        d = device_inputs(wl)
+        pa.reshape_and_cache(d["hist_key"], d["hist_value"], d["k_cache"], d["v_cache"],
+                             d["hist_slots"], wl.k_scale, wl.v_scale)
+        kw = dict(scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale, partition_size=P)
+        k1, v1 = d["k_cache"].clone(), d["v_cache"].clone()
+        pa.reshape_and_cache(d["new_key"], d["new_value"], k1, v1, d["new_slots"], wl.k_scale,
+                             wl.v_scale)
+        sep = pa.decode(d["q"], k1, v1, d["block_tables"], d["context_lens"], **kw)
+        k2, v2 = d["k_cache"].clone(), d["v_cache"].clone()
+        fused = pa.decode_append(d["q"], d["new_key"], d["new_value"], k2, v2,
+                                 d["block_tables"], d["context_lens"], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(k1, k2) and torch.equal(v1, v2)
+        assert np.array_equal(W.to_numpy(k2), kc) and np.array_equal(W.to_numpy(v2), vc)
+        assert torch.equal(sep, fused)
+        assert_close(W.widen_to_f64(fused), ref, "bf16", f"int8 bs={bs} append P={P}")
 
 
 def test_long_ctx_int8_b8():

@@ -20,6 +20,7 @@ from .configs import (
     tiny_fp32_gqa2,
     permute_physical,
     unshare,
+    with_scale_tables,
     PrefillWorkload,
     PREFILL_BUILDERS,
     prefill_custom,
@@ -47,6 +48,7 @@ __all__ = [
     "prefill_custom",
     "prefill_llama3_8b_b8",
     "unshare",
+    "with_scale_tables",
     "to_device",
     "to_numpy",
     "widen_to_f64",

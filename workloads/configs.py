@@ -87,6 +87,12 @@ class Workload:
     # sequences share blocks
     prefix_members: Optional[np.ndarray] = None
     prefix_lens: Optional[np.ndarray] = None
+    # 8-bit caches with scale tables instead of per-tensor scales: the layout
+    # (1 per KV head [Hkv], 2 per block [NB], 3 per (block, KV head)
+    # [NB, Hkv]; 0: per-tensor k_scale / v_scale) and float32 tables
+    scale_layout: int = 0
+    k_scales: Optional[np.ndarray] = None
+    v_scales: Optional[np.ndarray] = None
     info: Dict = field(default_factory=dict)
 
     @property
@@ -445,6 +451,49 @@ def custom(ctx_lens, Hq, Hkv, d, q_dtype="bf16", kv_dtype="bf16", bs=16, seed=0,
 
 
 # ---------------------------------------------------------------------------
+# scale tables for 8-bit caches
+# ---------------------------------------------------------------------------
+
+def with_scale_tables(wl: Workload, layout: int) -> Workload:
+    """The same workload with its 8-bit cache quantised through scale tables
+    of the given layout (1 per KV head, 2 per physical block, 3 per (block,
+    KV head)) instead of one scale per tensor.
+
+    The tables are a caller's calibration, fixed before any write: each
+    entry is amax|x| / code_max over the K (resp. V) values of every token
+    the step writes into that block and head (history and new tokens),
+    rounded to float32 (code_max 448 for E4M3FN, 127 for int8); an entry no
+    token reaches is 1.0. The pool holds no other values (it starts empty and
+    is filled by the step's writes)."""
+    assert wl.kv_dtype in CODE_MAX and wl.hist_slots is not None
+    nb, hkv = wl.num_blocks, wl.num_kv_heads
+    slots = np.concatenate([wl.hist_slots, wl.new_slots[wl.new_slots >= 0]])
+    blk = slots // wl.block_size
+    cmax = np.float32(CODE_MAX[wl.kv_dtype])
+
+    def table(hist, new):
+        rows = np.concatenate([hist, new[wl.new_slots >= 0]])
+        x = _bf16_as_f32(rows) if rows.dtype == np.uint16 else rows.astype(np.float32)
+        per_row = np.abs(x).max(axis=2)                 # [N, Hkv]
+        amax = np.zeros((nb, hkv), np.float32)
+        np.maximum.at(amax, blk, per_row)
+        if layout == 1:
+            keep = amax.max(axis=0)
+        elif layout == 2:
+            keep = amax.max(axis=1)
+        else:
+            keep = amax
+        keep = np.asarray(keep, np.float32)
+        return np.where(keep > 0, keep / cmax, np.float32(1.0)).astype(np.float32)
+
+    zeros = np.zeros_like(wl.k_cache)
+    return replace(wl, name=f"{wl.name}_scales{layout}", scale_layout=int(layout),
+                   k_scales=table(wl.hist_key, wl.new_key),
+                   v_scales=table(wl.hist_value, wl.new_value),
+                   k_cache=zeros, v_cache=zeros.copy(), k_scale=1.0, v_scale=1.0)
+
+
+# ---------------------------------------------------------------------------
 # relabelings used by the invariance tests
 # ---------------------------------------------------------------------------
 
@@ -468,6 +517,9 @@ def permute_physical(wl: Workload, seed: int) -> Workload:
         block_tables=perm[wl.block_tables].astype(np.int32),
         cow_pairs=perm[wl.cow_pairs].astype(np.int64).reshape(-1, 2),
         hist_slots=slots(wl.hist_slots), new_slots=slots(wl.new_slots),
+        # per-block scale tables move with their blocks
+        k_scales=wl.k_scales[inv].copy() if wl.scale_layout in (2, 3) else wl.k_scales,
+        v_scales=wl.v_scales[inv].copy() if wl.scale_layout in (2, 3) else wl.v_scales,
     )
 
 
