@@ -108,11 +108,16 @@ def decode_bytes(wl):
     entries of the blocks attended."""
     kv_tok = 2 * wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
     q_bytes = wl.q.size * ELEM_BYTES[wl.q_dtype]
-    tables = sum(-(-int(n) // wl.block_size) for n in wl.context_lens) * 4
+    blocks = sum(-(-int(n) // wl.block_size) for n in wl.context_lens)
+    tables = blocks * 4
     kv = wl.tokens_attended * kv_tok
-    return {"kv": kv, "kv_per_token": kv_tok, "q": q_bytes, "out": q_bytes, "tables": tables,
-            "ctx_lens": 4 * wl.num_seqs,
-            "total": kv + 2 * q_bytes + tables + 4 * wl.num_seqs}
+    # scale tables (K and V, float32): per attended block and KV head, per
+    # attended block, or per KV head
+    scales = {0: 0, 1: 8 * wl.num_kv_heads, 2: 8 * blocks,
+              3: 8 * blocks * wl.num_kv_heads}[wl.scale_layout]
+    return {"kv": kv, "kv_per_token": kv_tok, "q": q_bytes, "out": q_bytes,
+            "tables": tables + scales, "ctx_lens": 4 * wl.num_seqs,
+            "total": kv + 2 * q_bytes + tables + scales + 4 * wl.num_seqs}
 
 
 def unique_kv_bytes(wl):
@@ -226,16 +231,26 @@ def cpu_baseline(wl, budget_s):
     import oracle
 
     kc, vc = wl.k_cache.copy(), wl.v_cache.copy()  # the workload's own arrays stay as built
+    blk = {}
+    if wl.scale_layout:
+        nb, hkv = wl.num_blocks, wl.num_kv_heads
+        blk = dict(k_block_scales=oracle.expand_scales(wl.k_scales, wl.scale_layout, nb, hkv),
+                   v_block_scales=oracle.expand_scales(wl.v_scales, wl.scale_layout, nb, hkv))
     done_tokens, done_seqs, t_used = 0, 0, 0.0
     order = [int(b) for b in np.random.default_rng(0).permutation(wl.num_seqs)]
     while t_used < budget_s:
         b = order[done_seqs % len(order)]
         t0 = time.perf_counter()
         if wl.new_slots is not None and wl.new_slots[b] >= 0:
-            oracle.reshape_and_cache(wl.new_key[b:b + 1], wl.new_value[b:b + 1], kc, vc,
-                                     wl.new_slots[b:b + 1], wl.k_scale, wl.v_scale)
+            if wl.scale_layout:
+                oracle.reshape_and_cache_scaled(wl.new_key[b:b + 1], wl.new_value[b:b + 1], kc,
+                                                vc, wl.new_slots[b:b + 1], wl.k_scales,
+                                                wl.v_scales, wl.scale_layout)
+            else:
+                oracle.reshape_and_cache(wl.new_key[b:b + 1], wl.new_value[b:b + 1], kc, vc,
+                                         wl.new_slots[b:b + 1], wl.k_scale, wl.v_scale)
         oracle.paged_decode(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale,
-                            wl.k_scale, wl.v_scale, seqs=[b])
+                            wl.k_scale, wl.v_scale, seqs=[b], **blk)
         t_used += time.perf_counter() - t0
         done_tokens += int(wl.context_lens[b])
         done_seqs += 1
@@ -319,10 +334,19 @@ class Prepared:
         self.new_v = t(wl.new_value) if wl.new_value is not None else None
         self.new_s = t(wl.new_slots) if wl.new_slots is not None else None
         k0, v0 = t(wl.k_cache), t(wl.v_cache)
+        # scale tables of an 8-bit cache (shared by the layer copies: the
+        # writes below use every block's scales, never change them)
+        self.ks = t(wl.k_scales) if wl.scale_layout else None
+        self.vs = t(wl.v_scales) if wl.scale_layout else None
         if wl.hist_slots is not None and len(wl.hist_slots):
-            pa.copy_blocks(k0, v0, self.cow)
-            pa.reshape_and_cache(t(wl.hist_key), t(wl.hist_value), k0, v0, t(wl.hist_slots),
-                                 wl.k_scale, wl.v_scale)
+            if wl.scale_layout:
+                pa.copy_blocks_scaled(k0, v0, self.ks, self.vs, wl.scale_layout, self.cow)
+                pa.reshape_and_cache_scaled(t(wl.hist_key), t(wl.hist_value), k0, v0,
+                                            t(wl.hist_slots), self.ks, self.vs, wl.scale_layout)
+            else:
+                pa.copy_blocks(k0, v0, self.cow)
+                pa.reshape_and_cache(t(wl.hist_key), t(wl.hist_value), k0, v0,
+                                     t(wl.hist_slots), wl.k_scale, wl.v_scale)
         self.layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(layers - 1)]
         self.out = torch.empty_like(self.q)
         self.gm = self.pl = self.ws_sp = None
@@ -354,8 +378,29 @@ class Prepared:
 
         def fn(i):
             kc, vc = self.layers[i % len(self.layers)]
-            pa.decode(self.q, kc, vc, self.bt, self.cl, scale=wl.scale, k_scale=wl.k_scale,
-                      v_scale=wl.v_scale, partition_size=P, out=self.out, workspace=ws)
+            if wl.scale_layout:
+                pa.decode_scaled(self.q, kc, vc, self.bt, self.cl, self.ks, self.vs,
+                                 wl.scale_layout, scale=wl.scale, partition_size=P,
+                                 out=self.out, workspace=ws)
+            else:
+                pa.decode(self.q, kc, vc, self.bt, self.cl, scale=wl.scale, k_scale=wl.k_scale,
+                          v_scale=wl.v_scale, partition_size=P, out=self.out, workspace=ws)
+        return fn
+
+    def write_fn(self):
+        """The slot write of the step's new tokens."""
+        import paged_kv_cache_426_amd as pa
+
+        wl = self.wl
+
+        def fn(i):
+            kc, vc = self.layers[i % len(self.layers)]
+            if wl.scale_layout:
+                pa.reshape_and_cache_scaled(self.new_k, self.new_v, kc, vc, self.new_s, self.ks,
+                                            self.vs, wl.scale_layout)
+            else:
+                pa.reshape_and_cache(self.new_k, self.new_v, kc, vc, self.new_s, wl.k_scale,
+                                     wl.v_scale)
         return fn
 
     def shared_fn(self):
@@ -430,7 +475,7 @@ def measure_config(wl, dev, args, stream, cpu_seconds):
         "frac": alg / pair_s / 1e9 / HBM_PEAK_GBPS,
         "traffic": committed_traffic(wl.name, P),
     }
-    if P:
+    if P and not wl.scale_layout:  # (no partials entry point for scale tables)
         fn, arg = prep.partials_fn(P)
         ps = avg_launch_s(fn, n, stream)
         e["partials_only_us"] = ps * 1e6
@@ -451,14 +496,10 @@ def measure_config(wl, dev, args, stream, cpu_seconds):
     # a1: the slot write of the step's new tokens; a2: the copy-on-write copies
     import paged_kv_cache_426_amd as pa
     if prep.new_s is not None:
-        def wfn(i):
-            kc, vc = prep.layers[i % len(prep.layers)]
-            pa.reshape_and_cache(prep.new_k, prep.new_v, kc, vc, prep.new_s, wl.k_scale,
-                                 wl.v_scale)
-        wt = avg_launch_s(wfn, 200, stream)
+        wt = avg_launch_s(prep.write_fn(), 200, stream)
         e["slot_write"] = {"us": wt * 1e6, "tokens": int((wl.new_slots >= 0).sum()),
                            "bytes": write_bytes(wl), "gbps": write_bytes(wl) / wt / 1e9}
-    if len(wl.cow_pairs):
+    if len(wl.cow_pairs) and not wl.scale_layout:
         def cfn(i):
             kc, vc = prep.layers[i % len(prep.layers)]
             pa.copy_blocks(kc, vc, prep.cow)
@@ -569,7 +610,19 @@ def measure_prefill(name, dev, args, stream, cpu_seconds):
 
 
 PER_CONFIG = ("tiny_fp32_gqa2", "llama3_8b_b32", "mha_b32_ctx4096", "shared_prefix_cow_b64",
-              "long_ctx_fp8_b8", "long_ctx_int8_b8")
+              "long_ctx_fp8_b8", "long_ctx_int8_b8",
+              "long_ctx_fp8_b8_scales3", "long_ctx_int8_b8_scales3")
+
+
+def build_config(name):
+    """A workload by name; a `_scales<L>` suffix: the same workload with scale
+    tables of layout L (an 8-bit cache) instead of per-tensor scales."""
+    import workloads as W
+
+    m = re.match(r"(.*)_scales(\d)$", name)
+    if m:
+        return W.with_scale_tables(W.build(m.group(1)), int(m.group(2)))
+    return W.build(name)
 
 
 def main(argv=None):
@@ -783,7 +836,7 @@ def main(argv=None):
         per = []
         for name in PER_CONFIG:
             t1 = time.perf_counter()
-            w = wl if name == wl.name else W.build(name)
+            w = wl if name == wl.name else build_config(name)
             e = measure_config(w, dev, args, stream,
                                0.0 if args.no_cpu_baseline else args.cpu_seconds_per_config)
             log(f"per-config {name}: decode {e['decode_us']:.2f} us, {e['frac'] * 100:.1f} % of "

@@ -181,8 +181,9 @@ pa_status pa_decode_reduce(void *out, const float *tmp_out, const float *max_log
     return PA_ERR_BAD_SHAPE;
   if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
     return PA_ERR_UNSUPPORTED;
-  if (num_seqs > 65535 || num_q_heads > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // merge grids: (sequences, head runs of 256 / head_dim) or (heads, sequences)
+  if (num_seqs > 65535 || num_q_heads > 65535 * (256 / head_dim)) return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % 16 != 0) return PA_ERR_BAD_SHAPE;
   if (partition_size < 0) {
     if (num_seqs > pa::kMaxBalancedSeqs || partition_size < -pa::kMaxAutoSplits)

@@ -3,6 +3,9 @@
 // themselves are in pa_decode_kernel.h, instantiated one element-type pair per
 // translation unit.
 
+#include <limits.h>
+#include <stdint.h>
+
 #include <map>
 #include <mutex>
 #include <utility>
@@ -121,6 +124,91 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReducePara
   store_elem<OT>(p.out, bh * D + d, O / W);
 }
 
+// Merge of a fixed split: one workgroup per (query head, sequence), its four
+// waves taking the sequence's partitions in turn (partition i to wave i % 4),
+// so that a wave issues the loads of up to kFixedMergeBatch partitions at
+// once and long contexts cost one memory round trip per batch rather than
+// per partition; each lane holds D / 64 elements of the output row. The
+// waves' (max, weight, sum) triples are then merged in LDS in wave order.
+constexpr int kFixedMergeWaves = 4;
+constexpr int kFixedMergeBatch = 16;
+
+template <int OT, int D>
+__global__ __launch_bounds__(kFixedMergeWaves * kWave) void reduce_fixed_kernel(
+    const ReduceParams p) {
+  constexpr int EPL = D / kWave;  // output elements per lane
+  constexpr int NWV = kFixedMergeWaves;
+  constexpr int R = kFixedMergeBatch;
+  __shared__ float s_m[NWV], s_w[NWV];
+  __shared__ float s_o[NWV][D];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = p.context_lens[b];
+  const int np = (num_blocks_of(n) + p.partition_blocks - 1) / p.partition_blocks;
+  const size_t bh = (size_t)b * p.num_q_heads + h;
+  if (np == 0) {
+    for (int i = threadIdx.x; i < D; i += NWV * kWave) store_elem<OT>(p.out, bh * D + i, 0.0f);
+    return;
+  }
+  if (np == 1 && p.skip_single) return;
+  const size_t base = bh * p.max_partitions;
+  float M = -INFINITY, W = 0.0f, O[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) O[e] = 0.0f;
+  for (int i0 = wave; i0 < np; i0 += NWV * R) {
+    float mm[R], ll[R], tt[R][EPL];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int i = i0 + u * NWV;
+      const bool ok = i < np;
+      mm[u] = ok ? p.max_logits[base + i] : -INFINITY;
+      ll[u] = ok ? p.exp_sums[base + i] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) tt[u][e] = ok ? p.tmp_out[(base + i) * D + lane * EPL + e] : 0.0f;
+    }
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < R; ++u) bm = fmaxf(bm, mm[u]);
+    const float rs = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - bm) * kLog2e);
+    W *= rs;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[e] *= rs;
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      if (i0 + u * NWV < np) {
+        const float w = ll[u] * __builtin_amdgcn_exp2f((mm[u] - bm) * kLog2e);
+        W += w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) O[e] = fmaf(w, tt[u][e], O[e]);
+      }
+    M = bm;
+  }
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_w[wave] = W;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_o[wave][lane * EPL + e] = O[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) Mx = fmaxf(Mx, s_m[w]);
+  float Wt = 0.0f, Ot[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) Ot[e] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    // a wave that took no partition has M = -inf and weight 0
+    const float sc = s_m[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((s_m[w] - Mx) * kLog2e);
+    Wt += s_w[w] * sc;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) Ot[e] = fmaf(s_o[w][lane * EPL + e], sc, Ot[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_elem<OT>(p.out, bh * D + lane * EPL + e, Ot[e] / Wt);
+}
+
 KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, int kind, bool append,
                             bool large, bool scaled) {
 #define PA_PAIR(Q, KV, NAME)                                                                   \
@@ -139,6 +227,7 @@ KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, int kind, 
 }
 
 }  // namespace
+
 
 // Workgroups of one decode kernel that fill a device once: compute units x
 // resident workgroups per unit. Looked up once per (device, kernel) and kept
@@ -190,6 +279,31 @@ BalancedChoice balanced_kernel(const DecodeLaunch &a, bool append, bool large) {
           false, (int)rows};
 }
 
+// The single-pass / fixed-split kernel of a launch. A fixed split runs one
+// wave per head row (each workgroup reads whole cache blocks: all of their
+// KV heads) where the head rows fill eight-wave workgroups and that kernel
+// is built; a single pass, with one workgroup per sequence and head-row
+// group, would leave the device mostly idle that way, and keeps two-wave
+// workgroups per head row.
+struct FixedChoice {
+  KernelRef k;
+  bool row_waves;
+};
+
+FixedChoice fixed_kernel(const DecodeLaunch &a, bool append, bool large, bool scaled) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int gh = heads_per_workgroup(group);
+  const long long rows = (long long)a.num_kv_heads * (group / gh);
+  if (a.mode == kSplitFixed && rows % 8 == 0) {
+    const KernelRef k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRowWaves,
+                                          append, large, scaled);
+    if (k.fn) return {k, true};
+  }
+  return {decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRanges, append, large,
+                            scaled),
+          false};
+}
+
 int balanced_num_splits(const DecodeLaunch &a) {
   const BalancedChoice c = balanced_kernel(a, false, false);
   if (!c.k.fn) return 2;
@@ -229,6 +343,7 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.num_splits = a.num_splits;
   const bool wide = p.mode == kSplitBalanced;
   p.direct = a.direct;
+  p.swz_rows = 0;
   p.group = a.num_q_heads / a.num_kv_heads;
   const bool q8 = a.kv_dtype == PA_FP8_E4M3FN || a.kv_dtype == PA_INT8;
   // scale tables: each block's scales are applied per block in the kernel
@@ -259,10 +374,21 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
     grid = c.row_waves ? dim3(p.num_splits, c.rowgroups, 1)
                        : dim3((p.num_splits + 1) / 2, head_groups, 1);
   } else {
-    k = decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRanges, append, large,
-                          scaled);
-    grid = a.mode == kSplitFixed ? dim3(a.max_partitions, head_groups, a.num_seqs)
-                                 : dim3(1, head_groups, a.num_seqs);
+    const FixedChoice c = fixed_kernel(a, append, large, scaled);
+    k = c.k;
+    const int y = c.row_waves ? head_groups / 8 : head_groups;
+    grid = a.mode == kSplitFixed ? dim3(a.max_partitions, y, a.num_seqs) : dim3(1, y, a.num_seqs);
+    // a fixed split runs on a one-dimensional grid that spreads every
+    // sequence's partitions over the XCDs (see decode_kernel)
+    if (a.mode == kSplitFixed && k.fn) {
+      const long long xp = (a.max_partitions + 7LL) / 8 * 8;
+      const long long n = xp * a.num_seqs * y;
+      // (the dispatch packet counts work-items in 32 bits)
+      if (n * k.threads <= (long long)UINT32_MAX) {
+        p.swz_rows = y;
+        grid = dim3((unsigned)n, 1, 1);
+      }
+    }
   }
   if (!k.fn) return (int)hipErrorInvalidValue;
   void *args[] = {&p};
@@ -289,6 +415,23 @@ int launch_reduce(const ReduceLaunch &a, void *stream) {
   const int hpw = kReduceThreads / a.head_dim;
   const dim3 grid(a.num_seqs, (a.num_q_heads + hpw - 1) / hpw);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.mode == kSplitFixed) {
+    const dim3 fgrid(a.num_q_heads, a.num_seqs);
+#define PA_REDF(OT, D)                                                                         \
+  if (a.out_dtype == OT && a.head_dim == D) {                                                  \
+    hipLaunchKernelGGL((reduce_fixed_kernel<OT, D>), fgrid, dim3(kFixedMergeWaves * kWave), 0, \
+                       s, p);                                                                  \
+    return (int)hipGetLastError();                                                             \
+  }
+    PA_REDF(PA_F32, 64)
+    PA_REDF(PA_F32, 128)
+    PA_REDF(PA_F16, 64)
+    PA_REDF(PA_F16, 128)
+    PA_REDF(PA_BF16, 64)
+    PA_REDF(PA_BF16, 128)
+#undef PA_REDF
+    return (int)hipErrorInvalidValue;
+  }
 #define PA_RED(OT, D)                                                                          \
   if (a.out_dtype == OT && a.head_dim == D) {                                                  \
     hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(kReduceThreads), 0, s, p);          \

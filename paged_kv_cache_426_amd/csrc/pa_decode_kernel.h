@@ -99,6 +99,9 @@ struct DecodeParams {
   int max_partitions;    // stride of the partial arrays (see DecodeLaunch)
   int num_splits;        // balanced: number of shares S
   int direct;            // a range that is a whole sequence writes `out` directly
+  // fixed split on a one-dimensional grid (0: grid (partitions, rows,
+  // sequences)): the number of head-row groups; see decode_kernel
+  int swz_rows;
   int group;             // query heads per KV head
   float scale_log2;      // scale * k_scale * log2(e)
   float v_scale;
@@ -983,7 +986,9 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   #pragma unroll
         for (int e = 0; e < 8; ++e) store_elem<QT>(p.out, bh * D + d0 + e, x[e] * inv);
       } else {
-        const size_t pi = (size_t)(h0 + h) * p.max_partitions + piece;
+        const size_t pi = (p.mode == kSplitBalanced)
+                              ? (size_t)(h0 + h) * p.max_partitions + piece
+                              : bh * p.max_partitions + piece;
         float *dst = p.tmp_out + pi * D + d0;
         *reinterpret_cast<f32x4 *>(dst) =
             f32x4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
@@ -1216,13 +1221,29 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(const DecodeParams p
   int first_b = 0, first_n = 0, first_lo = 0, first_hi = 0, first_piece = 0;
   bool first_whole = false;
   if (p.mode != kSplitBalanced) {
-    const int h0 = blockIdx.y * GH;  // first query head of this workgroup
-    const int b = blockIdx.z;
-    const int part = blockIdx.x;
+    // first query head of this workgroup (RW: of this wave, one head row per wave)
+    // Fixed split on a one-dimensional grid: workgroup L runs on XCD L % 8;
+    // of sequence b, XCD r takes the partitions with partition % 8 ==
+    // (r + b) % 8, so that every XCD gets about an eighth of every
+    // sequence's partitions whatever the length mix (with a grid indexed by
+    // partition, XCD r would take every partition p % 8 == r, and the XCDs
+    // of high partition numbers would idle on short sequences). Within a
+    // sequence and head-row group, consecutive workgroups take consecutive
+    // partitions.
+    int part = blockIdx.x, row = blockIdx.y, b = blockIdx.z;
+    if (p.swz_rows > 0) {
+      const int L = blockIdx.x, r = L & 7, q = L >> 3;
+      const int xqn = (p.max_partitions + 7) >> 3;
+      const int t = q / xqn;
+      row = t % p.swz_rows;
+      b = t / p.swz_rows;
+      part = 8 * (q % xqn) + ((r + b) & 7);
+    }
+    const int h0 = RW ? (row * NW + uniform(tid >> 6)) * GH : row * GH;
     const int n = p.context_lens[b];
     if (n <= 0) {
       if (p.mode == kSplitSingle)
-        for (int i = tid; i < GH * D; i += (NW * kWave))
+        for (int i = RW ? (tid & (kWave - 1)) : tid; i < GH * D; i += (RW ? kWave : NW * kWave))
           store_elem<QT>(p.out, ((size_t)b * p.num_q_heads + h0) * D + i, 0.0f);
       return;
     }

@@ -202,6 +202,11 @@ def test_partials_and_reduce_validation():
                               NULL) == 3
     assert L.pa_decode_reduce(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 0, 16, pa.PA_F32, NULL) == 2
     assert L.pa_decode_reduce(NULL, FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 4, 16, pa.PA_F32, NULL) == 1
+    # merge launch-grid limits
+    assert L.pa_decode_reduce(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4 * 65536, 64, 4, 16, pa.PA_F32,
+                              NULL) == 3
+    assert L.pa_decode_reduce(FAKE, FAKE, FAKE, FAKE, FAKE, 65536, 4, 64, 4, 16, pa.PA_F32,
+                              NULL) == 3
 
 
 def test_reshape_and_copy_validation():
