@@ -72,6 +72,8 @@ constexpr int kStages = 2;  // register stages of the load pipeline
 // per compute unit where the registers allow (see balanced_waves).
 constexpr int kFixedWaves = 2;
 constexpr float kLog2e = 1.4426950408889634f;
+// lazy softmax reference maximum: probabilities stay below 2^kLazyMax
+constexpr float kLazyMax = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -374,6 +376,7 @@ struct Shared {
   float alpha[NW][GH];          // rescale factor of the current unit
   float m[NW][GH];              // per-wave softmax state at the end of a range
   float l[NW][GH];
+  float mt[NW][GH];             // per-wave true maxima at the end of a range
   float acc[NW][GH][D];
   // K tiles of the current unit, one per wave and block
   uint8_t kt[NW][NBI][kBs * (D * ElemBytes<KT>::value + 16)] __attribute__((aligned(16)));
@@ -685,7 +688,9 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   };
 
   // ---- per-wave softmax state ----------------------------------------------
-  float m[4], l[4];
+  // m: reference maximum (lazy, see compute_unit), l: sum of exp2(s - m),
+  // mt: the lane's true running maximum
+  float m[4], l[4], mt[4];
   // P.V on MFMA for 4 to 16 query heads of a 128-wide head (16-bit queries;
   // per block of the unit): 16x16x16 products per 16 output columns replace the
   // GH x 8 fp32 FMAs per V element on the vector ALU (rows past GH repeat
@@ -704,6 +709,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       m[v] = -INFINITY;
+      mt[v] = -INFINITY;
       l[v] = 0.0f;
     }
     if constexpr (PVM) {
@@ -818,34 +824,53 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       sv[bi][2] = ok ? d.z * lf[bi] : -INFINITY;
       sv[bi][3] = ok ? d.w * lf[bi] : -INFINITY;
     }
-    // online softmax per MFMA row v (head (4*jq + v) % GH)
-    float al[4];
+    // Online softmax per MFMA row v (head (4*jq + v) % GH), with a lazy
+    // reference maximum: m moves only when a logit passes it by more than
+    // kLazyMax (log2 domain), so the probabilities exp2(s - m) stay below
+    // 2^kLazyMax. Most units move no row: then the row reductions, the
+    // rescale factors and the rescale of the sums and accumulators are
+    // skipped (a wave-wide decision). m stays at most the true running
+    // maximum, and a partial's (m, l, o) means the same for any such m.
+    float lm[4];
+    bool up = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float mx = sv[0][v];
+      lm[v] = sv[0][v];
 #pragma unroll
-      for (int bi = 1; bi < NBI; ++bi) mx = fmaxf(mx, sv[bi][v]);
-      mx = group_max<16>(mx);
-      const float mn = fmaxf(m[v], mx);
-      al[v] = __builtin_amdgcn_exp2f(m[v] - mn);
-      m[v] = mn;
+      for (int bi = 1; bi < NBI; ++bi) lm[v] = fmaxf(lm[v], sv[bi][v]);
+      up = up || lm[v] > m[v] + kLazyMax;
+      mt[v] = fmaxf(mt[v], lm[v]);
+    }
+    const bool any_up = __builtin_amdgcn_ballot_w64(up) != 0;
+    float al[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (any_up) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float mn = fmaxf(m[v], group_max<16>(lm[v]));
+        al[v] = __builtin_amdgcn_exp2f(m[v] - mn);
+        m[v] = mn;
+        l[v] *= al[v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
       float sum = 0.0f;
 #pragma unroll
       for (int bi = 0; bi < NBI; ++bi) {
-        const float e = __builtin_amdgcn_exp2f(sv[bi][v] - mn);
+        const float e = __builtin_amdgcn_exp2f(sv[bi][v] - m[v]);
         sv[bi][v] = e;
         sum += e;
       }
-      l[v] = l[v] * al[v] + sum;
+      l[v] += sum;
     }
-    // hand the probabilities and alpha to the V layout
+    // hand the probabilities (and alpha) to the V layout
     if (4 * jq < GH) {
 #pragma unroll
       for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (v < GH) sh.p[wave][bi * kBs + tl][4 * jq + v] = SC ? sv[bi][v] * vsc[bi] : sv[bi][v];
-      if (tl == 0) {
+      if (!PVM && any_up && tl == 0) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (v < GH) sh.alpha[wave][4 * jq + v] = al[v];
@@ -854,12 +879,14 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     wave_lds_fence();
     if constexpr (PVM) {
       // rows 4 jq + j of acc2 are this lane's softmax rows: alpha in hand
+      if (any_up) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        acc2[t].x *= al[0];
-        acc2[t].y *= al[1];
-        acc2[t].z *= al[2];
-        acc2[t].w *= al[3];
+        for (int t = 0; t < 8; ++t) {
+          acc2[t].x *= al[0];
+          acc2[t].y *= al[1];
+          acc2[t].z *= al[2];
+          acc2[t].w *= al[3];
+        }
       }
 #pragma unroll
       for (int bi = 0; bi < NBI; ++bi) {
@@ -911,7 +938,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       }
       }
     } else {
-      {
+      if (any_up) {
         float a[GH];
 #pragma unroll
         for (int h = 0; h < GH; ++h) a[h] = sh.alpha[wave][h];
@@ -975,11 +1002,25 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   // end of a range with one wave per head row (RW): the wave alone holds the
   // range's softmax state and writes its heads' partial (or the output, for
   // a whole sequence) with no exchange between waves
-  auto epilogue_wave = [&](int b, int piece, bool whole, int h0) {
+  // end of a range: the sums over a row's token lanes (against the
+  // reference maximum m) and the row's true maximum. Partials carry the
+  // range's true maximum Mt and l scaled to it, l * exp2(m - Mt) (a wave
+  // with no unit in the range has l = 0 and m = Mt = -inf).
+  auto row_totals = [&]() {
   #pragma unroll
-    for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
+    for (int v = 0; v < 4; ++v) {
+      l[v] = group_sum<16>(l[v]);
+      mt[v] = group_max<16>(mt[v]);
+    }
+  };
+  auto to_true_max = [](float L, float M, float Mt) {
+    return Mt == -INFINITY ? 0.0f : L * __builtin_amdgcn_exp2f(M - Mt);
+  };
+
+  auto epilogue_wave = [&](int b, int piece, bool whole, int h0) {
+    row_totals();
     const bool to_out = whole && p.direct;
-    auto put = [&](int h, int d0, const float (&x)[8], float M, float L) {
+    auto put = [&](int h, int d0, const float (&x)[8], float M, float L, float Mt) {
       const size_t bh = (size_t)b * Hq + h0 + h;
       const float inv = p.v_scale / L;
       if (to_out) {
@@ -995,8 +1036,8 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
         *reinterpret_cast<f32x4 *>(dst + 4) =
             f32x4{x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv};
         if (d0 == 0) {
-          p.max_logits[pi] = M * kLn2;
-          p.exp_sums[pi] = L;
+          p.max_logits[pi] = Mt * kLn2;
+          p.exp_sums[pi] = to_true_max(L, M, Mt);
         }
       }
     };
@@ -1010,7 +1051,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   #pragma unroll
           for (int t = 0; t < 8; ++t)
             x[t] = v == 0 ? acc2[t].x : v == 1 ? acc2[t].y : v == 2 ? acc2[t].z : acc2[t].w;
-          put(4 * jq + v, 8 * tl, x, m[v], l[v]);
+          put(4 * jq + v, 8 * tl, x, m[v], l[v], mt[v]);
         }
       }
     } else {
@@ -1020,6 +1061,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
           if (v < GH) {
             sh.m[wave][4 * jq + v] = m[v];
             sh.l[wave][4 * jq + v] = l[v];
+            sh.mt[wave][4 * jq + v] = mt[v];
           }
       }
   #pragma unroll
@@ -1031,7 +1073,8 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       wave_lds_fence();
       if (r == 0) {
   #pragma unroll
-        for (int h = 0; h < GH; ++h) put(h, 8 * c, acc[h], sh.m[wave][h], sh.l[wave][h]);
+        for (int h = 0; h < GH; ++h)
+          put(h, 8 * c, acc[h], sh.m[wave][h], sh.l[wave][h], sh.mt[wave][h]);
       }
       wave_lds_fence();
     }
@@ -1045,14 +1088,14 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       return;
     }
     // merge the waves: sums over the token lanes / rows, then across waves
-  #pragma unroll
-    for (int v = 0; v < 4; ++v) l[v] = group_sum<16>(l[v]);
+    row_totals();
     if (4 * jq < GH && tl == 0) {
   #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (v < GH) {
           sh.m[wave][4 * jq + v] = m[v];
           sh.l[wave][4 * jq + v] = l[v];
+          sh.mt[wave][4 * jq + v] = mt[v];
         }
     }
     if constexpr (PVM) {
@@ -1106,8 +1149,11 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
                               : bh * p.max_partitions + piece;
         p.tmp_out[pi * D + d] = res;
         if (d == 0) {
-          p.max_logits[pi] = M * kLn2;
-          p.exp_sums[pi] = L;
+          float Mt = -INFINITY;
+  #pragma unroll
+          for (int w = 0; w < NW; ++w) Mt = fmaxf(Mt, sh.mt[w][h]);
+          p.max_logits[pi] = Mt * kLn2;
+          p.exp_sums[pi] = to_true_max(L, M, Mt);
         }
       }
     }
