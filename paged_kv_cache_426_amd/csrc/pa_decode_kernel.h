@@ -204,6 +204,24 @@ __device__ __forceinline__ void buf_load_v(VPiece<KT> &pc, __amdgpu_buffer_rsrc_
   }
 }
 
+// Byte n of w as a signed int8 code, in float (exact; one sign-extending
+// byte-select conversion).
+__device__ __forceinline__ float int8_byte(uint32_t w, int n) {
+  return (float)(int)(signed char)(w >> (8 * n));
+}
+
+// Two floats that are exact in the query's 16-bit type, packed (low, high).
+template <int QT>
+__device__ __forceinline__ uint32_t pack16_exact(float lo, float hi) {
+  if constexpr (QT == PA_BF16) {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(__bf16)lo, (__bf16)hi});
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
+  }
+}
+
 // 8 V elements -> fp32; all zero when the token is masked.
 template <int KT>
 __device__ __forceinline__ void widen_v(const VPiece<KT> &pc, bool ok, float (&x)[8]) {
@@ -230,7 +248,7 @@ __device__ __forceinline__ void widen_v(const VPiece<KT> &pc, bool ok, float (&x
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[4 * i + k] = (float)((int32_t)(w[i] << (24 - 8 * k)) >> 24);
+      for (int k = 0; k < 4; ++k) x[4 * i + k] = int8_byte(w[i], k);
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -258,13 +276,7 @@ __device__ __forceinline__ uint32_t fp8_pair_to_16(uint32_t w) {
 // 16-bit type: codes are integers of at most 8 significant bits.
 template <int QT, bool HI>
 __device__ __forceinline__ uint32_t int8_pair_to_16(uint32_t w) {
-  const float f0 = (float)((int32_t)(w << (HI ? 8 : 24)) >> 24);
-  const float f1 = (float)((int32_t)(w << (HI ? 0 : 16)) >> 24);
-  if constexpr (QT == PA_BF16) {
-    return (f2u(f0) >> 16) | (f2u(f1) & 0xffff0000u);
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1));
-  }
+  return pack16_exact<QT>(int8_byte(w, HI ? 2 : 0), int8_byte(w, HI ? 3 : 1));
 }
 
 // B operand of MFMA step s from the lane's K loads of one block.
@@ -920,18 +932,19 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
           const uint32_t sel = (t % 2) ? 0x07060302u : 0x05040100u;
           bop.x = __builtin_amdgcn_perm(pcs[1].w[t / 2], pcs[0].w[t / 2], sel);
           bop.y = __builtin_amdgcn_perm(pcs[3].w[t / 2], pcs[2].w[t / 2], sel);
+        } else if constexpr (KT == PA_INT8) {
+          // byte t of tokens (i0, i1), each converted straight from its word
+          bop.x = pack16_exact<QT>(int8_byte(pcs[0].w[t / 4], t % 4),
+                                   int8_byte(pcs[1].w[t / 4], t % 4));
+          bop.y = pack16_exact<QT>(int8_byte(pcs[2].w[t / 4], t % 4),
+                                   int8_byte(pcs[3].w[t / 4], t % 4));
         } else {
           // byte t of tokens (i0, i1) into bytes 0, 1, widened exactly
           const uint32_t sel = 0x0c0c0000u | ((4u + t % 4) << 8) | (uint32_t)(t % 4);
           const uint32_t w01 = __builtin_amdgcn_perm(pcs[1].w[t / 4], pcs[0].w[t / 4], sel);
           const uint32_t w23 = __builtin_amdgcn_perm(pcs[3].w[t / 4], pcs[2].w[t / 4], sel);
-          if constexpr (KT == PA_INT8) {
-            bop.x = int8_pair_to_16<QT, false>(w01);
-            bop.y = int8_pair_to_16<QT, false>(w23);
-          } else {
-            bop.x = fp8_pair_to_16<QT, false>(w01);
-            bop.y = fp8_pair_to_16<QT, false>(w23);
-          }
+          bop.x = fp8_pair_to_16<QT, false>(w01);
+          bop.y = fp8_pair_to_16<QT, false>(w23);
         }
         acc2[t] = mfma16<QT>(aop, bop, acc2[t]);
         acc2[t] = mfma16<QT>(aol, bop, acc2[t]);
