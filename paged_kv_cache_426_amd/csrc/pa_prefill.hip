@@ -171,7 +171,13 @@ void prefill_kernel(const PrefillParams p) {
   constexpr int TQ = kPrefillRows / GH;       // chunk tokens per workgroup
   constexpr int KB = ElemBytes<KT>::value;    // cache element bytes
   constexpr int KRS = D * 2 + 16;             // LDS row stride of the K tile (16-bit)
-  constexpr int VRS = kPrefillKeys * 2 + 16;  // LDS row stride of the V^T tile
+  // V^T tile in LDS: row d (element) holds the step's 32 keys, 16-bit, in a
+  // row of 18 dwords; key pair c (keys 2c, 2c + 1) sits at dword c ^ vsw(d),
+  // vsw(d) = 8 ((d / 16) & 1). With this stride the 16 rows a half-wave
+  // reads (8 bytes each, same columns) fall in distinct banks, and with the
+  // swizzle the 32 words a half-wave writes (8 key pairs of 4 element
+  // groups, see vkp and vdg) do too.
+  constexpr int VRS = kPrefillKeys * 2 + 8;
   constexpr int NST = D / 32;                 // MFMA k-steps over the head dimension
   constexpr int NDT = D / 16;                 // 16-column tiles of the output
   constexpr int DG = D / 8;                   // 8-element pieces of a row
@@ -277,8 +283,12 @@ void prefill_kernel(const PrefillParams p) {
   // thread roles: K pieces (key, 8-element group); V key pairs (2 keys, 8 elements)
   u32x4 kreg[KPIECES];
   u32x4 vreg[2];
-  const int vkp = tid / DG, vdg = tid % DG;  // V: key pair, element group
-  const bool vrole = vkp < kPrefillKeys / 2;
+  // V: key pair and element group. Wave w takes the key pairs of half w % 2
+  // of the step (8 pairs, fastest over the lanes) and element groups
+  // 8 (w / 2) .. 8 (w / 2) + 7.
+  const int vkp = 8 * (wave & 1) + (lane & 7);
+  const int vdg = 8 * (wave >> 1) + (lane >> 3);
+  const bool vrole = vdg < DG;
   // The keys a wave loads lie in one 16-key half of the step (64 lanes cover
   // 4 or 8 consecutive keys of K, 8 or 16 of V, aligned), so each load's
   // buffer resource is wave-uniform (a per-lane resource would make the
@@ -325,7 +335,8 @@ void prefill_kernel(const PrefillParams p) {
         // element e of both keys, side by side (low half: the even key)
         const uint32_t sel = (e % 2) ? 0x07060302u : 0x05040100u;
         const uint32_t w = __builtin_amdgcn_perm(cw[e / 2], aw[e / 2], sel);
-        *reinterpret_cast<uint32_t *>(&vsm[bf][(vdg * 8 + e) * VRS + key * 2]) = w;
+        const int d = vdg * 8 + e;
+        *reinterpret_cast<uint32_t *>(&vsm[bf][d * VRS + 4 * (vkp ^ (8 * ((d >> 4) & 1)))]) = w;
       }
     }
   };
@@ -377,9 +388,11 @@ void prefill_kernel(const PrefillParams p) {
     u32x4 va[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      // (rows 16 dt .. 16 dt + 15 share the swizzle: the two key halves
+      // trade places in odd tiles)
       const uint8_t *vr = &vsm[bf][(16 * dt + tl) * VRS];
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 8 * jq);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 32 + 8 * jq);
+      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 8 * jq + 32 * (dt & 1));
+      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 8 * jq + 32 * (1 - (dt & 1)));
       va[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
     u32x4 pb[2];
