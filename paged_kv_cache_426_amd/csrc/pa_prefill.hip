@@ -41,6 +41,7 @@
 // or NaN cache contents never reach the result).
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <math.h>
 
 #include "pa_device.h"
@@ -398,10 +399,9 @@ void prefill_kernel(const PrefillParams p) {
     u32x4 pb[2];
     float alpha[2] = {1.0f, 1.0f};
     float sv[2][8];
-    bool ok[2][8];
     float lm[2];  // this lane's largest scaled logit of the step, per block
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const f32x4 x = st[kt][c];
@@ -410,23 +410,31 @@ void prefill_kernel(const PrefillParams p) {
         sv[c][4 * kt + 2] = x.z;
         sv[c][4 * kt + 3] = x.w;
       }
+    // key i of block c is visible to the block's row (always, in a step
+    // without the mask: those steps carry no mask arithmetic)
+    auto visible = [&](auto mask_tag, int c, int i) {
+      return !decltype(mask_tag)::value || k0 + 16 * (i / 4) + 4 * jq + i % 4 <= pos[c];
+    };
+    auto lane_max = [&](auto mask_tag) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        ok[c][i] = !diag || k0 + 16 * (i / 4) + 4 * jq + i % 4 <= pos[c];
-      // the largest scaled logit: the largest raw logit times a positive
-      // scale, the smallest times a negative or zero one; masked keys never win
-      float e;
-      if (pos_scale) {
-        e = -INFINITY;
+      for (int c = 0; c < 2; ++c) {
+        // the largest scaled logit: the largest raw logit times a positive
+        // scale, the smallest times a negative or zero one; masked keys never win
+        float e;
+        if (pos_scale) {
+          e = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e = fmaxf(e, ok[c][i] ? sv[c][i] : -INFINITY);
-      } else {
-        e = INFINITY;
+          for (int i = 0; i < 8; ++i) e = fmaxf(e, visible(mask_tag, c, i) ? sv[c][i] : -INFINITY);
+        } else {
+          e = INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e = fminf(e, ok[c][i] ? sv[c][i] : INFINITY);
+          for (int i = 0; i < 8; ++i) e = fminf(e, visible(mask_tag, c, i) ? sv[c][i] : INFINITY);
+        }
+        lm[c] = __builtin_isinf(e) ? -INFINITY : e * sl2;
       }
-      lm[c] = __builtin_isinf(e) ? -INFINITY : e * sl2;
-    }
+    };
+    if (diag) lane_max(std::true_type{});
+    else lane_max(std::false_type{});
     // A row's reference maximum m moves only when the row's maximum exceeds
     // it by more than 8: unless some lane's own maximum does, no row moves
     // and the row reductions are skipped (the usual case once every row has
@@ -449,22 +457,26 @@ void prefill_kernel(const PrefillParams p) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[c][dt] *= alpha[c];
     }
+    auto probs = [&](auto mask_tag) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // a row that has seen no key yet keeps m = -inf and gets no weight
-      const float mref = m[c] == -INFINITY ? 0.0f : m[c];
-      float sum = 0.0f;
-      float pr[8];
+      for (int c = 0; c < 2; ++c) {
+        // a row that has seen no key yet keeps m = -inf and gets no weight
+        const float mref = m[c] == -INFINITY ? 0.0f : m[c];
+        float sum = 0.0f;
+        float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sv[c][i], sl2, -mref));
-        pr[i] = ok[c][i] ? e : 0.0f;
-        sum += pr[i];
+        for (int i = 0; i < 8; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sv[c][i], sl2, -mref));
+          pr[i] = visible(mask_tag, c, i) ? e : 0.0f;
+          sum += pr[i];
+        }
+        l[c] += sum;
+        pb[c] = u32x4{pack16<QT>(pr[0], pr[1]), pack16<QT>(pr[2], pr[3]),
+                      pack16<QT>(pr[4], pr[5]), pack16<QT>(pr[6], pr[7])};
       }
-      l[c] += sum;
-      pb[c] = u32x4{pack16<QT>(pr[0], pr[1]), pack16<QT>(pr[2], pr[3]),
-                    pack16<QT>(pr[4], pr[5]), pack16<QT>(pr[6], pr[7])};
-    }
+    };
+    if (diag) probs(std::true_type{});
+    else probs(std::false_type{});
     // O^T += V^T P^T per 16 output columns
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
