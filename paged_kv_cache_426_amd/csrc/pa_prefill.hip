@@ -289,7 +289,8 @@ void prefill_kernel(const PrefillParams p) {
   // 8 (w / 2) .. 8 (w / 2) + 7.
   const int vkp = 8 * (wave & 1) + (lane & 7);
   const int vdg = 8 * (wave >> 1) + (lane >> 3);
-  const bool vrole = vdg < DG;
+  // (every thread has a V role when the element groups fill the waves)
+  const bool vrole = (DG * kPrefillKeys / 2 == kPrefillWaves * kWave) || vdg < DG;
   // The keys a wave loads lie in one 16-key half of the step (64 lanes cover
   // 4 or 8 consecutive keys of K, 8 or 16 of V, aligned), so each load's
   // buffer resource is wave-uniform (a per-lane resource would make the
@@ -353,12 +354,18 @@ void prefill_kernel(const PrefillParams p) {
   const float sl2 = p.scale_log2;
   const bool pos_scale = sl2 > 0.0f;
 
+  // Step s + 1's K/V are stored to LDS at the end of step s, between its
+  // P.V MFMAs (the other buffer was last read in step s - 1, which every
+  // wave has finished at step s's barrier), and its loads go out right
+  // after that barrier. Past the last step both load nothing (zero-length
+  // buffer ranges) and store zeros to the unused buffer, so the step has no
+  // branches around them.
   issue(0);
+  stash(0, 0);
   for (int s = 0; s < nsteps; ++s) {
     const int bf = s & 1;
-    stash(s, bf);
     __syncthreads();
-    if (s + 1 < nsteps) issue(s + 1);
+    issue(s + 1);
     const int k0 = kPrefillKeys * s;
     // S^T = K Q^T for both 16-key tiles and both column blocks
     f32x4 st[2][2];
@@ -477,11 +484,19 @@ void prefill_kernel(const PrefillParams p) {
     };
     if (diag) probs(std::true_type{});
     else probs(std::false_type{});
-    // O^T += V^T P^T per 16 output columns
+    // O^T += V^T P^T per 16 output columns, interleaved with the store of
+    // step s + 1's K/V
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) o[c][dt] = mfma32<QT>(va[dt], pb[c], o[c][dt]);
+    stash(s + 1, bf ^ 1);
+#pragma unroll
+    for (int i = 0; i < 2 * NDT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);  // two vector-ALU
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+    }
   }
 
   // ---- normalise and write: lane holds row (c, tl), elements 16 dt + 4 jq + 0..3
