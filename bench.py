@@ -88,6 +88,8 @@ def parse_args(argv=None):
                     help="wall-clock budget of the CPU oracle sample of each per-config entry")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill batch (pa_prefill) and print its JSON object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (a known byte count for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -645,6 +647,14 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    if args.prefill_only:
+        e = measure_prefill("prefill_llama3_8b_b8", dev, args, stream, 0.0)
+        log(f"prefill_llama3_8b_b8: {e['prefill_us']:.1f} us, "
+            f"{e['roofline']['achieved']:.0f} TFLOP/s = {e['roofline']['frac'] * 100:.1f} % of "
+            f"{MFMA_BF16_PEAK_TFLOPS:.0f}")
+        print(json.dumps({"prefill": e}), flush=True)
+        return 0
+
     t0 = time.perf_counter()
     kw = {} if args.partition_size is None else {"partition_size": args.partition_size}
     if args.block_size is not None:
@@ -753,7 +763,8 @@ def main(argv=None):
         kname = ("shared-prefix decode: prep, prefix-pass and suffix-pass decode kernels and "
                  "merge, timed together, against the distinct K/V bytes")
     elif P:
-        kname = "decode launch pair: decode_kernel (split partials) + reduce_kernel (merge)"
+        kname = ("decode launch pair: decode_kernel (split partials) + the merge kernel "
+                 "(reduce_fixed_kernel for fixed partitions, reduce_kernel for the balanced split)")
     else:
         kname = "decode_kernel (single pass)"
     roof = {
