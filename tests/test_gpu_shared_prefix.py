@@ -111,6 +111,15 @@ def test_wide_inputs(mbs, Hq, q_dtype):
     _check(wl, members, pl, f"mbs={mbs} Hq={Hq} {q_dtype}")
 
 
+def test_many_sequences():
+    """1000 sequences, 60 of them in 30 groups of two, the rest in no group
+    (whole contexts through the suffix pass, some empty)."""
+    wl, members, pl = _forked(30, 2, 48, [1, 9, 20], 8, 2, 64, seed=13,
+                              loners=[5, 0, 37, 130] * 235)
+    assert wl.num_seqs == 1000
+    _check(wl, members, pl, "1000 sequences, 30 groups")
+
+
 @pytest.mark.parametrize("bs", [32, 64])
 def test_large_blocks(bs):
     wl, members, pl = _forked(2, 4, 256, [9, 100], 32, 8, 128, bs=bs, seed=bs)
