@@ -656,13 +656,15 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   constexpr bool appending = APP;
   auto load_app = [&](const Seg &sg) {
     AR a;
-    const int n = sg.n;
+    // wave-uniform values, stated as such so that the descriptors below
+    // stay scalar (see issue)
+    const int n = uniform(sg.n);
     const int lb = n > 0 ? (n - 1) / kBs : 0;
     const bool here = appending && sg.valid && n > 0 && lb >= sg.blo && lb < sg.bhi;
     a.blk = here ? lb : -1;
     a.t = n > 0 ? (n - 1) % kBs : 0;
-    const int b = sg.valid ? sg.b : 0;
-    const size_t rowoff = ((size_t)b * p.num_kv_heads + sg.g) * D * AR::qb;
+    const int b = uniform(sg.valid ? sg.b : 0);
+    const size_t rowoff = ((size_t)b * p.num_kv_heads + uniform(sg.g)) * D * AR::qb;
     const uint32_t bytes = here ? (uint32_t)(D * AR::qb) : 0u;
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(appending ? p.new_k + rowoff : p.q, bytes);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(appending ? p.new_v + rowoff : p.q, bytes);
@@ -745,7 +747,12 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
 
   // Loads of one unit of KV head g into a register stage: the unit whose
   // block ids start at lane u * NBI of `ids`; an invalid unit loads nothing.
-  auto issue = [&](const Ids &ids, int u, bool valid, int g, St &st) {
+  auto issue = [&](const Ids &ids, int u, bool valid, int g_in, St &st) {
+    // g is the same in every lane; in several instantiations (scale tables,
+    // d = 64, larger blocks, workgroups sharing ranges among waves) the
+    // compiler otherwise loses track of that and wraps every buffer load of
+    // the unit in a loop over the distinct descriptor values of the wave
+    const int g = uniform(g_in);
     // head g's row 0 to the block end
     const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;
 #pragma unroll
