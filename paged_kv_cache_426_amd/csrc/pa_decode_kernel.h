@@ -857,7 +857,7 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
       lm[v] = sv[0][v];
 #pragma unroll
       for (int bi = 1; bi < NBI; ++bi) lm[v] = fmaxf(lm[v], sv[bi][v]);
-      up = up || lm[v] > m[v] + kLazyMax;
+      up |= lm[v] > m[v] + kLazyMax;  // not ||: no per-lane branches
       mt[v] = fmaxf(mt[v], lm[v]);
     }
     const bool any_up = __builtin_amdgcn_ballot_w64(up) != 0;
