@@ -326,12 +326,20 @@ void prefill_kernel(const PrefillParams p) {
     }
     if (vrole) {
       const int key = 2 * vkp;
-      const bool ok0 = kPrefillKeys * s + key <= plast;
-      const bool ok1 = kPrefillKeys * s + key + 1 <= plast;
       const u32x4 a = widen8<QT, KT>(vreg[0]);
       const u32x4 c = widen8<QT, KT>(vreg[1]);
-      const uint32_t aw[4] = {ok0 ? a.x : 0u, ok0 ? a.y : 0u, ok0 ? a.z : 0u, ok0 ? a.w : 0u};
-      const uint32_t cw[4] = {ok1 ? c.x : 0u, ok1 ? c.y : 0u, ok1 ? c.z : 0u, ok1 ? c.w : 0u};
+      uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+      uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+      // only a step that reaches past the last position has keys to zero
+      if (kPrefillKeys * s + kPrefillKeys - 1 > plast) {
+        const bool ok0 = kPrefillKeys * s + key <= plast;
+        const bool ok1 = kPrefillKeys * s + key + 1 <= plast;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          aw[e] = ok0 ? aw[e] : 0u;
+          cw[e] = ok1 ? cw[e] : 0u;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // element e of both keys, side by side (low half: the even key)
@@ -418,9 +426,12 @@ void prefill_kernel(const PrefillParams p) {
         sv[c][4 * kt + 3] = x.w;
       }
     // key i of block c is visible to the block's row (always, in a step
-    // without the mask: those steps carry no mask arithmetic)
+    // without the mask: those steps carry no mask arithmetic): its position
+    // k0 + 4 jq + 16 (i / 4) + i % 4 is at most the row's, i.e. the
+    // constant 16 (i / 4) + i % 4 is at most pos[c] - k0 - 4 jq
     auto visible = [&](auto mask_tag, int c, int i) {
-      return !decltype(mask_tag)::value || k0 + 16 * (i / 4) + 4 * jq + i % 4 <= pos[c];
+      if constexpr (!decltype(mask_tag)::value) return true;
+      else return 16 * (i / 4) + i % 4 <= pos[c] - k0 - 4 * jq;
     };
     auto lane_max = [&](auto mask_tag) {
 #pragma unroll
