@@ -230,8 +230,9 @@ KernelRef decode_kernel_for(int q_dtype, int kv_dtype, int d, int gh, int kind, 
 
 
 // Workgroups of one decode kernel that fill a device once: compute units x
-// resident workgroups per unit. Looked up once per (device, kernel) and kept
-// for the life of the process (a device property, not state of a call).
+// resident workgroups per unit (one for four-wave kernels, see below). Looked
+// up once per (device, kernel) and kept for the life of the process (a
+// device property, not state of a call).
 int fill_workgroups(const void *fn, int threads) {
   static std::mutex mu;
   static std::map<std::pair<int, const void *>, int> cache;
@@ -250,7 +251,11 @@ int fill_workgroups(const void *fn, int threads) {
     (void)hipGetLastError();
     return 0;
   }
-  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  // Four-wave kernels (16 heads per workgroup, most fp32) fit two per unit,
+  // but one per unit with twice the shares each measured faster (the
+  // hardware serves co-resident workgroups unevenly; shared-prefix call 53.7
+  // -> 51.3 us, while a third of the shares or fewer leaves units idle).
+  const int n = cus * (per_cu <= 0 ? 1 : threads <= 4 * kWave ? 1 : per_cu);
   cache[key] = n;
   return n;
 }
