@@ -161,10 +161,17 @@ __global__ __launch_bounds__(kFixedMergeWaves * kWave) void reduce_fixed_kernel(
     for (int u = 0; u < R; ++u) {
       const int i = i0 + u * NWV;
       const bool ok = i < np;
-      mm[u] = ok ? p.max_logits[base + i] : -INFINITY;
-      ll[u] = ok ? p.exp_sums[base + i] : 0.0f;
+      // loads of partition 0 (always present) in place of a missing one,
+      // then a select: no branch around each load
+      const size_t col = base + (ok ? i : 0);
+      const float mv = p.max_logits[col], lv = p.exp_sums[col];
+      mm[u] = ok ? mv : -INFINITY;
+      ll[u] = ok ? lv : 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) tt[u][e] = ok ? p.tmp_out[(base + i) * D + lane * EPL + e] : 0.0f;
+      for (int e = 0; e < EPL; ++e) {
+        const float tv = p.tmp_out[col * D + lane * EPL + e];
+        tt[u][e] = ok ? tv : 0.0f;
+      }
     }
     float bm = M;
 #pragma unroll
