@@ -128,10 +128,11 @@ int pa_num_partitions(int max_blocks_per_seq, int block_size, int partition_size
 /*
  * Share count of the automatic balanced split (partition_size = -1) on the
  * current device for this head and type configuration: the number of
- * workgroups that fill every compute unit once at the decode kernel's
- * occupancy, divided by the workgroups per share (num_kv_heads * query-head
- * runs), at least 2 and at most 2048. Returns 0 for an unsupported
- * configuration. Queries the device (HIP runtime) on first use.
+ * workgroups that fill every compute unit once (one workgroup per unit for
+ * the four-wave kernels, which measured faster than two; as many as fit
+ * otherwise), divided by the workgroups per share (num_kv_heads *
+ * query-head runs), at least 2 and at most 2048. Returns 0 for an
+ * unsupported configuration. Queries the device (HIP runtime) on first use.
  */
 int pa_decode_balanced_splits(int num_q_heads, int num_kv_heads, int head_dim, int q_dtype,
                               int kv_dtype);
