@@ -47,11 +47,15 @@
  * Supported configurations: head_dim 64 or 128; block_size 16, 32, 64, 128
  * or 256 for decode (the pages give 16 as the usual size and suggest 16 to
  * 128, or 64 to 256: "PagedAttention deep dive" section 2.1, "KV-cache
- * sharing article" sections 2 and 4), any block size for the slot write and
- * the block copy; any num_q_heads that is a multiple of num_kv_heads; (q, kv)
- * element types (f32, f32), (f16, f16), (bf16, bf16), (f16, fp8_e4m3fn),
- * (bf16, fp8_e4m3fn), (f16, int8), (bf16, int8). Decode reads a block of
- * 16 * 2^k tokens as 2^k consecutive 16-token sub-blocks.
+ * sharing article" sections 2 and 4), and also 8 for pa_decode,
+ * pa_decode_partials, pa_decode_noalloc and pa_decode_shared_prefix (not for
+ * pa_decode_append, pa_decode_scaled or pa_prefill: PA_ERR_UNSUPPORTED); any
+ * block size for the slot write and the block copy; any num_q_heads that is a
+ * multiple of num_kv_heads; (q, kv) element types (f32, f32), (f16, f16),
+ * (bf16, bf16), (f16, fp8_e4m3fn), (bf16, fp8_e4m3fn), (f16, int8),
+ * (bf16, int8). Decode reads a block of 16 * 2^k tokens as 2^k consecutive
+ * 16-token sub-blocks, and two consecutive 8-token blocks of a block table as
+ * one 16-token unit.
  */
 #ifndef PA_H
 #define PA_H
@@ -100,7 +104,9 @@ int pa_version(void);
  *
  *   0      single pass: one workgroup reads a sequence's whole context.
  *   P > 0  fixed split: partition p of sequence b covers logical tokens
- *          [p*P, min((p+1)*P, n)); P is a multiple of block_size.
+ *          [p*P, min((p+1)*P, n)); P is a multiple of block_size and
+ *          of 16 (else PA_ERR_BAD_SHAPE, or PA_ERR_UNSUPPORTED for a
+ *          multiple of 8 that is not one of 16).
  *   -S     balanced split with S >= 2 shares: the 16-token sub-blocks of
  *          all sequences (whatever the block size), taken end to end in
  *          sequence order (ceil(n_b / 16) of them for sequence b, T in

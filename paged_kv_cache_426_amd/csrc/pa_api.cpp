@@ -47,10 +47,13 @@ pa_status check_decode(const void *q, const void *k_cache, const void *v_cache,
     return PA_ERR_BAD_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
   if (!known_dtype(q_dtype) || !known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
-  if (!supported_head_dim(head_dim) || pa::sub_block_log2(block_size) < 0 ||
+  if (!supported_head_dim(head_dim) || !pa::decode_block_size_ok(block_size) ||
       !supported_decode_pair(q_dtype, kv_dtype))
     return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % block_size != 0) return PA_ERR_BAD_SHAPE;
+  // partitions are whole 16-token units of the kernels (8-token blocks: an
+  // even number of blocks)
+  if (partition_size > 0 && partition_size % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 && num_seqs > pa::kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
   if (isinf(scale)) return PA_ERR_BAD_SHAPE;  // NaN: the default scale
   if (quantised(kv_dtype) && (!isfinite(k_scale) || !isfinite(v_scale)))
@@ -366,6 +369,8 @@ pa_status pa_decode_scaled(void *out, const void *q, const void *k_cache, const 
       !pa::scale_strides(scale_layout, num_kv_heads, &t.block_stride, &t.head_stride))
     return PA_ERR_BAD_SHAPE;
   if (known_dtype(kv_dtype) && !quantised(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  // a 16-token unit of 8-token blocks would carry two blocks' scales
+  if (block_size == pa::kHalfBlockSize) return PA_ERR_UNSUPPORTED;
   return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, scale, q_dtype, kv_dtype, 1.0f, 1.0f, partition_size,
@@ -384,6 +389,8 @@ pa_status pa_decode_append(void *out, const void *q, const void *key, const void
   if (quantised(kv_dtype) &&
       (!isfinite(k_scale) || !isfinite(v_scale) || k_scale == 0.0f || v_scale == 0.0f))
     return PA_ERR_BAD_SHAPE;
+  // the appended row's slot is found in 16-token units (block sizes 16 to 256)
+  if (block_size == pa::kHalfBlockSize) return PA_ERR_UNSUPPORTED;
   return decode_impl(out, q, key, value, k_cache, v_cache, block_tables, context_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale,

@@ -345,12 +345,18 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.max_blocks_per_seq = a.max_blocks_per_seq;
-  // the kernels count 16-token sub-blocks; block_size is 16 << sub_log2
-  p.sub_log2 = sub_block_log2(a.block_size);
-  if (p.sub_log2 < 0) return (int)hipErrorInvalidValue;
+  // the kernels count 16-token units: sub-blocks of a block of 16 << sub_log2
+  // tokens, or pairs of 8-token blocks (kHalfBlocks; the SUB kernels)
+  const bool halves = a.block_size == kHalfBlockSize;
+  p.sub_log2 = halves ? kHalfBlocks : sub_block_log2(a.block_size);
+  if (!halves && p.sub_log2 < 0) return (int)hipErrorInvalidValue;
+  if (halves && (a.new_k != nullptr || a.k_scales != nullptr ||
+                 (a.mode == kSplitFixed && a.partition_size % kBs != 0)))
+    return (int)hipErrorInvalidValue;
   p.mode = a.mode;
-  p.partition_blocks = a.mode == kSplitSingle ? a.max_blocks_per_seq << p.sub_log2
-                                              : a.partition_size / kBs;
+  p.partition_blocks = a.mode != kSplitSingle ? a.partition_size / kBs
+                       : halves              ? (a.max_blocks_per_seq + 1) / 2
+                                             : a.max_blocks_per_seq << p.sub_log2;
   p.max_partitions = a.max_partitions;
   p.num_splits = a.num_splits;
   const bool wide = p.mode == kSplitBalanced;
@@ -376,7 +382,7 @@ int launch_decode(const DecodeLaunch &a, void *stream) {
   p.v_scale_w = a.v_scale;
   const int gh = heads_per_workgroup(p.group);
   const bool append = a.new_k != nullptr;
-  const bool large = p.sub_log2 > 0;
+  const bool large = p.sub_log2 != 0;
   const int head_groups = a.num_kv_heads * (p.group / gh);
   KernelRef k;
   dim3 grid;

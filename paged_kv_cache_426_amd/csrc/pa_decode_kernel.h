@@ -95,7 +95,9 @@ struct DecodeParams {
   int num_q_heads;
   int num_kv_heads;
   int max_blocks_per_seq;  // block-table row stride (physical blocks)
-  int sub_log2;            // log2(block_size / 16)
+  // log2(block_size / 16), or kHalfBlocks for 8-token blocks (kernels
+  // built with SUB only): a 16-token unit is then two physical blocks
+  int sub_log2;
   int mode;              // a SplitMode
   int partition_blocks;  // fixed / single: sub-blocks per partition
   int max_partitions;    // stride of the partial arrays (see DecodeLaunch)
@@ -509,7 +511,8 @@ struct Item {
 // Block ids of a segment's units, one per lane (see fetch_ids).
 struct Ids {
   int entry;  // block-table entry
-  int sub;    // 16-token sub-block within that block
+  int sub;    // 16-token sub-block within that block; with 8-token blocks,
+              // the unit's second block (its table entry, or -1 past the context)
   int ok;     // the lane holds a unit's block (scale tables only)
   float ks, vs;  // that block's K and V scales for the segment's KV head (scale tables only)
 };
@@ -637,8 +640,18 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     const bool ok = sg.valid && kk < sg.nk && j < sg.bhi;
     const int32_t *row = p.block_tables + (size_t)(sg.valid ? sg.b : 0) * p.max_blocks_per_seq;
     const int e = ok ? j : 0;
-    if constexpr (SUB) return Ids{row[e >> p.sub_log2], e & ((1 << p.sub_log2) - 1), ok, 0.f, 0.f};
-    else return Ids{row[e], 0, ok, 0.f, 0.f};
+    if constexpr (SUB) {
+      if (p.sub_log2 == kHalfBlocks) {
+        // 8-token blocks: the unit's rows 8..15 sit in the table's next
+        // entry, which exists only where the context reaches past row 7
+        const bool two = ok && 2 * e + 1 < (sg.n + 7) / 8;
+        const int second = row[two ? 2 * e + 1 : 0];
+        return Ids{row[2 * e], two ? second : -1, ok, 0.f, 0.f};
+      }
+      return Ids{row[e >> p.sub_log2], e & ((1 << p.sub_log2) - 1), ok, 0.f, 0.f};
+    } else {
+      return Ids{row[e], 0, ok, 0.f, 0.f};
+    }
   };
   // scale tables: each lane's block scales for KV head g, loaded where the
   // segment's ids are first used (their load is long done by then); lanes
@@ -745,6 +758,44 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   for (int i = 0; i < G::nvl; ++i) v_off[i] = (i * G::rv + r) * rowstride + c * G::v_piece;
   const float sl2 = p.scale_log2;
 
+  // Loads of a unit's rows 0..7 and 8..15 of KV head g from two cache
+  // ranges: byte offsets off0 and off1 of rows 0 and 8 (8-token blocks: two
+  // physical blocks, the second absent (has1 false) where the context ends
+  // before row 8; larger blocks: one sub-block, off1 = off0 + 8 rows). A load
+  // instruction of up to eight rows reads one range, chosen at compile time.
+  // A K load of sixteen rows (8-bit cache, d = 64) is issued once per range,
+  // each lane's offset pointing past the other range (2^31 bytes, above any
+  // block: checked on the host), where the load returns zeros, and the two
+  // results are or-ed.
+  auto issue_halves = [&](size_t off0, size_t off1, bool valid, bool has1, int g,
+                          u32x4 (&kst)[G::nkl], VPiece<KT> (&vst)[G::nvl]) {
+    const uint32_t back = (kBs / 2) * rowstride;
+    const uint32_t span = back - (uint32_t)g * G::row;
+    const __amdgpu_buffer_rsrc_t rk0 = block_rsrc(p.k_cache + off0, valid ? span : 0u);
+    const __amdgpu_buffer_rsrc_t rv0 = block_rsrc(p.v_cache + off0, valid ? span : 0u);
+    const __amdgpu_buffer_rsrc_t rk1 = block_rsrc(p.k_cache + off1, valid && has1 ? span : 0u);
+    const __amdgpu_buffer_rsrc_t rv1 = block_rsrc(p.v_cache + off1, valid && has1 ? span : 0u);
+    constexpr uint32_t kFar = 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < G::nkl; ++i) {
+      if constexpr (G::rvk <= kBs / 2) {
+        const int h = i * G::rvk / (kBs / 2);
+        kst[i] = buf_load16(h ? rk1 : rk0, k_off + i * G::rvk * rowstride - h * back);
+      } else {
+        const bool low = lane / G::lpk < kBs / 2;
+        const u32x4 a = buf_load16(rk0, low ? k_off : kFar);
+        const u32x4 b = buf_load16(rk1, low ? kFar : k_off - back);
+        kst[i] = u32x4{a.x | b.x, a.y | b.y, a.z | b.z, a.w | b.w};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G::nvl; ++i) {
+      static_assert(G::rv <= kBs / 2, "a V load reads rows of one 8-token block");
+      const int h = i * G::rv / (kBs / 2);
+      buf_load_v<KT>(vst[i], h ? rv1 : rv0, v_off[i] - h * back);
+    }
+  };
+
   // Loads of one unit of KV head g into a register stage: the unit whose
   // block ids start at lane u * NBI of `ids`; an invalid unit loads nothing.
   auto issue = [&](const Ids &ids, int u, bool valid, int g_in, St &st) {
@@ -759,8 +810,20 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     for (int bi = 0; bi < NBI; ++bi) {
       const int lidx = min(u * NBI + bi, kWave - 1);
       int id = __builtin_amdgcn_readlane(ids.entry, lidx);
-      if constexpr (SUB)  // the pool sub-block
-        id = (id << p.sub_log2) + __builtin_amdgcn_readlane(ids.sub, lidx);
+      if constexpr (SUB) {
+        const int sub = __builtin_amdgcn_readlane(ids.sub, lidx);
+        const size_t head = (size_t)g * G::row, half = (size_t)rowstride * (kBs / 2);
+        if (p.sub_log2 == kHalfBlocks) {
+          // two 8-token blocks
+          issue_halves((size_t)id * half + head, (size_t)(sub < 0 ? 0 : sub) * half + head, valid,
+                       sub >= 0, g, st.k[bi], st.v[bi]);
+        } else {
+          // the pool sub-block
+          const size_t off = (size_t)((id << p.sub_log2) + sub) * blk_bytes + head;
+          issue_halves(off, off + half, valid, true, g, st.k[bi], st.v[bi]);
+        }
+        continue;
+      }
       const size_t off = (size_t)id * blk_bytes + (size_t)g * G::row;
       const uint32_t n = valid ? blk_span : 0u;
       const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.k_cache + off, n);

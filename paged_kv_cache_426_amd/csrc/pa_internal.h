@@ -178,6 +178,14 @@ inline int sub_block_log2(int block_size) {
     if (block_size == (16 << k)) return k;
   return -1;
 }
+// 8-token blocks, which the decode kernels (pa_decode, pa_decode_partials,
+// pa_decode_noalloc) also take: a 16-token unit is then two physical blocks.
+// The decode parameters carry this value in place of log2(block_size / 16).
+constexpr int kHalfBlocks = -1;
+constexpr int kHalfBlockSize = 8;
+inline bool decode_block_size_ok(int block_size) {
+  return block_size == kHalfBlockSize || sub_block_log2(block_size) >= 0;
+}
 
 // heads of one KV group that one workgroup serves (a divisor of the group, <= 16)
 inline int heads_per_workgroup(int group) {

@@ -77,8 +77,9 @@ def _decode(**kw):
     (dict(out=NULL), 1), (dict(q=NULL), 1), (dict(bt=NULL), 1),
     (dict(Hq=3), 2),                               # Hq % Hkv != 0
     (dict(B=-1), 2), (dict(Hkv=0), 2), (dict(NB=0), 2), (dict(MBS=0), 2),
-    (dict(d=96), 3), (dict(bs=8), 3), (dict(bs=48), 3), (dict(bs=512), 3),
+    (dict(d=96), 3), (dict(bs=4), 3), (dict(bs=24), 3), (dict(bs=48), 3), (dict(bs=512), 3),
     (dict(bs=32, P=16), 2),                        # partition not a multiple of block_size
+    (dict(bs=8, P=24), 3),                         # partitions are whole 16-token units
     (dict(bs=256, NB=2 ** 28), 3),                 # 16-token sub-block ids exceed 32 bits
     (dict(qt=pa.PA_BF16, kt=pa.PA_F16), 3),        # mixed 16-bit types
     (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),  # fp8 cache needs a 16-bit query
@@ -106,8 +107,9 @@ def test_zero_sequences_is_a_no_op():
     assert _decode(B=0) == 0
     assert _decode(B=0, scale=float("nan")) == 0   # the default scale passes validation
     # int8 caches at every decode block size pass validation
-    for bs in (16, 32, 64, 128, 256):
+    for bs in (8, 16, 32, 64, 128, 256):
         assert _decode(B=0, qt=pa.PA_BF16, kt=pa.PA_INT8, bs=bs) == 0
+    assert _decode(B=0, bs=8, P=32, ws=FAKE, wsb=1 << 20) == 0
 
 
 def _scaled(**kw):
@@ -178,6 +180,7 @@ def _append(**kw):
     (dict(kt=pa.PA_FP8_E4M3FN, ks=0.0), 2),        # the new rows are quantised: scale != 0
     (dict(kt=pa.PA_FP8_E4M3FN, vs=float("nan")), 2),
     (dict(Hq=3), 2), (dict(d=96), 3),
+    (dict(bs=8), 3), (dict(bs=8, B=0), 3),          # 8-token blocks: decode without append
     (dict(P=16), 1),                               # split without workspace
     (dict(B=0), 0),                                # no sequences: no-op
 ])
@@ -252,7 +255,8 @@ def _shared(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(gm=NULL), 1), (dict(pl=NULL), 1), (dict(out=NULL), 1), (dict(ws=NULL), 1),
     (dict(G=0), 2), (dict(M=0), 2), (dict(Hq=30), 2),
-    (dict(G=1025), 3), (dict(B=1025), 3), (dict(d=96), 3), (dict(bs=8), 3),
+    (dict(G=1025), 3), (dict(B=1025), 3), (dict(d=96), 3), (dict(bs=4), 3), (dict(bs=24), 3),
+    (dict(bs=8), 4), (dict(bs=8, B=0), 0),          # 8-token blocks pass validation
     (dict(qt=pa.PA_F32, kt=pa.PA_FP8_E4M3FN), 3),
     (dict(Hq=65536 * 8, Hkv=65536), 3),            # stacked heads: launch grid limit
     (dict(), 4),                                   # workspace too small

@@ -132,3 +132,131 @@ def test_llama_shaped_batch_block_sizes():
     for placement in ("permuted", "contiguous"):
         wl = W.build("llama3_8b_b32", block_size=64, placement=placement)
         _check(wl, wl.partition_size, f"{wl.name}")
+
+
+# ---------------------------------------------------------------------------
+# 8-token blocks: a 16-token unit of the kernels is two consecutive table
+# entries (two unrelated physical blocks)
+# ---------------------------------------------------------------------------
+
+CTX8 = [1, 7, 8, 9, 15, 16, 17, 23, 24, 25, 63, 64, 65, 129, 255, 257, 511, 1025]
+
+
+def _as_8_token_blocks(wl):
+    """The same cache viewed as a pool of 8-token blocks: 16-token block e
+    is 8-token blocks 2e and 2e + 1, and entry j of a sequence's table is
+    2 * table[b][j // 2] + j % 2 (a slot is a row index: the same in both
+    views)."""
+    assert wl.block_size == 16
+    nb8 = wl.num_blocks * 2
+    kc = wl.k_cache.reshape(nb8, 8, *wl.k_cache.shape[2:])
+    vc = wl.v_cache.reshape(nb8, 8, *wl.v_cache.shape[2:])
+    j = np.arange(wl.block_tables.shape[1] * 2)
+    bt8 = (wl.block_tables[:, j // 2].astype(np.int64) * 2 + j % 2).astype(np.int32)
+    return replace(wl, block_size=8, num_blocks=nb8, k_cache=kc, v_cache=vc, block_tables=bt8)
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", PAIRS)
+def test_block_size_8_against_oracle(q_dtype, kv_dtype):
+    wl = W.custom(CTX8, 8, 2, 128, q_dtype=q_dtype, kv_dtype=kv_dtype, bs=8, seed=81)
+    for P in (0, 16, 48, -1, -5):
+        _check(wl, P, f"bs=8 {q_dtype}/{kv_dtype} P={P}")
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", [("f32", "f32"), ("f16", "f16"),
+                                              ("bf16", "fp8_e4m3fn"), ("f16", "int8")])
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 64), (32, 8, 128), (16, 1, 64)])
+def test_block_size_8_gqa_and_head_dim(q_dtype, kv_dtype, Hq, Hkv, d):
+    """Head dim 64 with an 8-bit cache is the case where one K load spans
+    sixteen token rows, i.e. both blocks of a unit."""
+    wl = W.custom([3, 9, 200, 705], Hq, Hkv, d, q_dtype=q_dtype, kv_dtype=kv_dtype, bs=8,
+                  seed=Hq + d)
+    for P in (0, 32, -1, -4):
+        _check(wl, P, f"bs=8 {q_dtype}/{kv_dtype} Hq={Hq} Hkv={Hkv} d={d} P={P}")
+
+
+@pytest.mark.parametrize("kv,d", [("bf16", 128), ("fp8_e4m3fn", 64), ("int8", 128),
+                                  ("int8", 64)])
+@pytest.mark.parametrize("P", [0, 32, -1, -7])
+def test_8_token_blocks_equal_their_16_token_pool_bitwise(kv, d, P):
+    wl16 = W.custom(CTX, 8, 2, d, q_dtype="bf16", kv_dtype=kv, bs=16, seed=5 + d)
+    wl8 = _as_8_token_blocks(wl16)
+    print(f"[block size] 8-token view of a 16-token pool, {kv} d={d} P={P}", flush=True)
+    _, out16 = device_step(wl16, P)
+    _, out8 = device_step(wl8, P)
+    torch.cuda.synchronize()
+    assert torch.equal(out8, out16)
+
+
+@pytest.mark.parametrize("P", [0, 32, -1, -4])
+def test_block_size_8_unused_entries_are_never_read(P):
+    """Every table entry past a sequence's last 8-token block names a
+    NaN-filled block, and so does the rest of each last block: where a
+    context ends in the first half of a 16-token unit, the unit's second
+    entry is one of those. The output is finite and bitwise the clean one."""
+    wl = W.custom([1, 8, 9, 17, 24, 40, 64, 100], 8, 2, 128, q_dtype="bf16", kv_dtype="bf16",
+                  bs=8, seed=6, extra_blocks=2)
+    kc, vc, _ = oracle_step(wl, decode=False)
+    clean = replace(wl, k_cache=kc, v_cache=vc, new_slots=None, new_key=None, new_value=None)
+    _, out_clean = device_step(clean, P)
+    nan16 = np.uint16(0x7FC0)
+    pk, pv = kc.copy(), vc.copy()
+    used = set()
+    for b, n in enumerate(wl.context_lens):
+        nblk = -(-int(n) // 8)
+        used.update(int(x) for x in wl.block_tables[b, :nblk])
+        last = wl.block_tables[b, nblk - 1]
+        pk[last, int(n) - (nblk - 1) * 8:] = nan16
+        pv[last, int(n) - (nblk - 1) * 8:] = nan16
+    poison = next(i for i in range(wl.num_blocks) if i not in used)
+    pk[poison] = nan16
+    pv[poison] = nan16
+    bt = wl.block_tables.copy()
+    for b, n in enumerate(wl.context_lens):
+        bt[b, -(-int(n) // 8):] = poison
+    print(f"[block size] bs=8 poisoned unused entries P={P}", flush=True)
+    _, out_dirty = device_step(replace(clean, k_cache=pk, v_cache=pv, block_tables=bt), P)
+    assert np.isfinite(W.widen_to_f64(out_dirty)).all()
+    assert torch.equal(out_dirty, out_clean)
+
+
+def test_block_size_8_partials_against_oracle():
+    """Balanced-split pieces count 16-token units with 8-token blocks too."""
+    S = 5
+    wl = W.custom([1, 95, 0, 96, 97, 400], 8, 2, 128, q_dtype="bf16", kv_dtype="bf16", bs=8,
+                  seed=31)
+    kc, vc, _ = oracle_step(wl, decode=False)
+    pieces = oracle.balanced_pieces(wl.context_lens, 16, S)
+    m, l, o = oracle.paged_decode_pieces(wl.q, kc, vc, wl.block_tables, wl.context_lens,
+                                         wl.scale, pieces, unit=16)
+    d = device_inputs(wl)
+    device_writes(wl, d)
+    print("[block size] bs=8 balanced partials", flush=True)
+    tmp, mx, es = pa.decode_partials(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                     d["context_lens"], -S, scale=wl.scale)
+    tmp_n, mx_n, es_n = (t.cpu().double().numpy() for t in (tmp, mx, es))
+    for i, (s, b, _, _) in enumerate(pieces):
+        col = s + b
+        assert np.abs(mx_n[:, col] - m[i]).max() <= 1e-4 * (1 + np.abs(m[i]).max())
+        assert np.allclose(es_n[:, col], l[i], rtol=1e-4, atol=1e-5)
+        assert np.allclose(tmp_n[:, col], o[i], rtol=1e-3, atol=1e-4)
+
+
+def test_block_size_8_entry_points_that_refuse_it():
+    wl = W.custom([9, 40], 8, 2, 128, q_dtype="bf16", kv_dtype="int8", bs=8, seed=2)
+    d = device_inputs(wl)
+    with pytest.raises(pa.PaError):
+        pa.decode_append(d["q"], d["new_key"], d["new_value"], d["k_cache"], d["v_cache"],
+                         d["block_tables"], d["context_lens"], scale=wl.scale,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale)
+    with pytest.raises(pa.PaError):
+        pa.decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                  scale=wl.scale, k_scale=wl.k_scale, v_scale=wl.v_scale, partition_size=24)
+
+
+@pytest.mark.parametrize("placement", ["permuted", "contiguous"])
+def test_llama_shaped_batch_block_size_8(placement):
+    """The Llama-shaped batch with 8-token blocks at the benchmark's launch
+    configuration."""
+    wl = W.build("llama3_8b_b32", block_size=8, placement=placement)
+    _check(wl, wl.partition_size, f"{wl.name}")

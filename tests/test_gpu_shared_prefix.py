@@ -126,6 +126,17 @@ def test_large_blocks(bs):
     _check(wl, members, pl, f"bs={bs}")
 
 
+@pytest.mark.parametrize("prompt", [160, 168])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_block_size_8(prompt, kv_dtype):
+    """8-token blocks: a prefix of an odd number of blocks ends in the first
+    half of a 16-token unit, and the suffix starts at the unit's second half."""
+    wl, members, pl = _forked(3, 4, prompt, [1, 8, 9, 100], 32, 8, 128, kv_dtype=kv_dtype,
+                              bs=8, seed=prompt)
+    assert (pl == prompt).all()
+    _check(wl, members, pl, f"bs=8 prompt={prompt} {kv_dtype}")
+
+
 def test_deterministic_and_workspace_contents_ignored():
     wl, members, pl = _forked(2, 4, 320, [3, 64, 129], 32, 8, 128, seed=5)
     d = device_inputs(wl)
