@@ -761,8 +761,11 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
   // Loads of a unit's rows 0..7 and 8..15 of KV head g from two cache
   // ranges: byte offsets off0 and off1 of rows 0 and 8 (8-token blocks: two
   // physical blocks, the second absent (has1 false) where the context ends
-  // before row 8; larger blocks: one sub-block, off1 = off0 + 8 rows). A load
-  // instruction of up to eight rows reads one range, chosen at compile time.
+  // before row 8; otherwise one 16-token block or sub-block, off1 = off0 + 8
+  // rows). A load instruction of up to eight rows reads one range, chosen at
+  // compile time. (One range per 16-token block measured 1.3 to 1.6 us slower
+  // per launch on the Llama-shaped batch, within the run-to-run spread on
+  // the other batches.)
   // A K load of sixteen rows (8-bit cache, d = 64) is issued once per range,
   // each lane's offset pointing past the other range (2^31 bytes, above any
   // block: checked on the host), where the load returns zeros, and the two
@@ -804,34 +807,23 @@ __device__ __forceinline__ void run_ranges(const DecodeParams &p,
     // compiler otherwise loses track of that and wraps every buffer load of
     // the unit in a loop over the distinct descriptor values of the wave
     const int g = uniform(g_in);
-    // head g's row 0 to the block end
-    const uint32_t blk_span = blk_bytes - (uint32_t)g * G::row;
+    const size_t head = (size_t)g * G::row, half = (size_t)rowstride * (kBs / 2);
 #pragma unroll
     for (int bi = 0; bi < NBI; ++bi) {
       const int lidx = min(u * NBI + bi, kWave - 1);
-      int id = __builtin_amdgcn_readlane(ids.entry, lidx);
-      if constexpr (SUB) {
+      const int id = __builtin_amdgcn_readlane(ids.entry, lidx);
+      if (SUB && p.sub_log2 == kHalfBlocks) {
+        // two 8-token blocks
         const int sub = __builtin_amdgcn_readlane(ids.sub, lidx);
-        const size_t head = (size_t)g * G::row, half = (size_t)rowstride * (kBs / 2);
-        if (p.sub_log2 == kHalfBlocks) {
-          // two 8-token blocks
-          issue_halves((size_t)id * half + head, (size_t)(sub < 0 ? 0 : sub) * half + head, valid,
-                       sub >= 0, g, st.k[bi], st.v[bi]);
-        } else {
-          // the pool sub-block
-          const size_t off = (size_t)((id << p.sub_log2) + sub) * blk_bytes + head;
-          issue_halves(off, off + half, valid, true, g, st.k[bi], st.v[bi]);
-        }
-        continue;
+        issue_halves((size_t)id * half + head, (size_t)(sub < 0 ? 0 : sub) * half + head, valid,
+                     sub >= 0, g, st.k[bi], st.v[bi]);
+      } else {
+        // a 16-token block, or a sub-block of a larger one
+        int sb = id;
+        if constexpr (SUB) sb = (id << p.sub_log2) + __builtin_amdgcn_readlane(ids.sub, lidx);
+        const size_t off = (size_t)sb * blk_bytes + head;
+        issue_halves(off, off + half, valid, true, g, st.k[bi], st.v[bi]);
       }
-      const size_t off = (size_t)id * blk_bytes + (size_t)g * G::row;
-      const uint32_t n = valid ? blk_span : 0u;
-      const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.k_cache + off, n);
-      const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.v_cache + off, n);
-#pragma unroll
-      for (int i = 0; i < G::nkl; ++i) st.k[bi][i] = buf_load16(rk, k_off + i * G::rvk * rowstride);
-#pragma unroll
-      for (int i = 0; i < G::nvl; ++i) buf_load_v<KT>(st.v[bi][i], rv, v_off[i]);
     }
   };
 
