@@ -63,6 +63,16 @@ def test_noalloc_single_pass_fp8_and_fp32():
     _both(W.build("tiny_fp32_gqa2"), 16)
 
 
+def test_noalloc_8_token_blocks():
+    """Two calls in a row over 8-token blocks, the second on a smaller batch."""
+    big = W.custom([9, 700, 1031, 64, 8], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", bs=8,
+                   seed=41)
+    small = W.custom([17, 1, 300], 32, 8, 128, q_dtype="bf16", kv_dtype="bf16", bs=8, seed=42)
+    for P in (-1, 32):
+        _both(big, P)
+        _both(small, P)
+
+
 def test_noalloc_refuses_partials_beyond_the_scratch():
     """1024 sequences with 512-token partitions of up to 256 of them need
     1024 * 32 * 256 * 130 * 4 bytes of partials, more than the scratch: the
