@@ -295,8 +295,8 @@ BalancedChoice balanced_kernel(const DecodeLaunch &a, bool append, bool large) {
 // wave per head row (each workgroup reads whole cache blocks: all of their
 // KV heads) where the head rows fill eight-wave workgroups and that kernel
 // is built; a single pass, with one workgroup per sequence and head-row
-// group, would leave the device mostly idle that way, and keeps two-wave
-// workgroups per head row.
+// group, would leave the device mostly idle that way, and runs four-wave
+// workgroups per head row (kKindSingle).
 struct FixedChoice {
   KernelRef k;
   bool row_waves;
@@ -311,7 +311,8 @@ FixedChoice fixed_kernel(const DecodeLaunch &a, bool append, bool large, bool sc
                                           append, large, scaled);
     if (k.fn) return {k, true};
   }
-  return {decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kKindRanges, append, large,
+  const int kind = a.mode == kSplitSingle ? kKindSingle : kKindRanges;
+  return {decode_kernel_for(a.q_dtype, a.kv_dtype, a.head_dim, gh, kind, append, large,
                             scaled),
           false};
 }

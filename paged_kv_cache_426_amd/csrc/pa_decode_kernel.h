@@ -67,10 +67,16 @@ namespace {
 
 constexpr int kBs = 16;  // tokens per cache block
 constexpr int kStages = 2;  // register stages of the load pipeline
-// Waves per workgroup (NW below): a fixed partition or a single sequence is
-// split between kFixedWaves waves; a balanced split runs one wide workgroup
-// per compute unit where the registers allow (see balanced_waves).
+// Waves per workgroup (NW below): a fixed partition is split between
+// kFixedWaves waves, a whole sequence (single pass) between kSingleWaves; a
+// balanced split runs one wide workgroup per compute unit where the
+// registers allow (see balanced_waves). A single pass has one workgroup per
+// sequence and head row, few for the device, so more waves share each range
+// (four against two: 302 against 587 us for 8 long sequences with 2 KV
+// heads, 64 against 87 us for the Llama-shaped batch); for fixed partitions
+// two waves measured as fast or faster (8-bit caches: 32 against 37 us).
 constexpr int kFixedWaves = 2;
+constexpr int kSingleWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 // lazy softmax reference maximum: probabilities stay below 2^kLazyMax
 constexpr float kLazyMax = 8.0f;
@@ -1501,9 +1507,9 @@ constexpr int balanced_waves() {
 
 // SUB: blocks larger than 16 tokens (read as 16-token sub-blocks); the
 // 16-token kernels leave the sub-block arithmetic out. kind is a KernelKind:
-// ranges (single pass or fixed partitions), balanced shares dealt to all
-// waves of a workgroup, or balanced shares with one wave per head row (built
-// where eight waves fit the registers; {nullptr, 0} otherwise).
+// fixed partitions, whole sequences (single pass), balanced shares dealt to
+// all waves of a workgroup, or balanced shares with one wave per head row
+// (built where eight waves fit the registers; {nullptr, 0} otherwise).
 template <int QT, int KT, int D, int GH, bool APP, bool SUB, bool SC>
 KernelRef kernel_of(int kind) {
   constexpr int NBI = units_of<QT, KT, GH>();
@@ -1519,6 +1525,10 @@ KernelRef kernel_of(int kind) {
     return {reinterpret_cast<const void *>(
                 &decode_kernel<QT, KT, D, GH, NBI, kStages, NWB, APP, SUB, false, SC>),
             NWB * kWave};
+  if (kind == kKindSingle)
+    return {reinterpret_cast<const void *>(
+                &decode_kernel<QT, KT, D, GH, NBI, kStages, kSingleWaves, APP, SUB, false, SC>),
+            kSingleWaves * kWave};
   return {reinterpret_cast<const void *>(
               &decode_kernel<QT, KT, D, GH, NBI, kStages, kFixedWaves, APP, SUB, false, SC>),
           kFixedWaves * kWave};

@@ -15,10 +15,10 @@ enum SplitMode : int {
   kSplitBalanced = 2,  // all sequences' blocks end to end, cut into num_splits equal shares
 };
 
-// Decode kernel variants: ranges (single pass, fixed partitions), balanced
-// shares dealt to all waves of a workgroup, balanced shares with one wave
-// per head row.
-enum KernelKind : int { kKindRanges = 0, kKindShares = 1, kKindRowWaves = 2 };
+// Decode kernel variants: ranges (fixed partitions), balanced shares dealt
+// to all waves of a workgroup, balanced shares with one wave per head row,
+// whole sequences (single pass; ranges over wider workgroups).
+enum KernelKind : int { kKindRanges = 0, kKindShares = 1, kKindRowWaves = 2, kKindSingle = 3 };
 
 // Balanced split: at most this many sequences per call (the per-sequence
 // start blocks live in LDS), and at most this many shares.
