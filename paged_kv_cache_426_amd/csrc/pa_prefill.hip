@@ -378,14 +378,19 @@ void prefill_kernel(const PrefillParams p) {
     __syncthreads();
     issue(s + 1);
     const int k0 = kPrefillKeys * s;
-    // S^T = K Q^T for both 16-key tiles and both column blocks
+    // S^T = K Q^T for both 16-key tiles and both column blocks: the four
+    // accumulators' chains are interleaved, k step by k step, so that
+    // consecutive MFMAs never depend on each other (two chains at a time,
+    // tile after tile, measured 3 % slower over the whole kernel)
     f32x4 st[2][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) st[kt][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ss = 0; ss < NST; ++ss) {
+    for (int ss = 0; ss < NST; ++ss) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
         const u32x4 a =
             *reinterpret_cast<const u32x4 *>(&ksm[bf][(kt * 16 + tl) * KRS + (32 * ss + 8 * jq) * 2]);
 #pragma unroll
